@@ -32,10 +32,10 @@ GENERATOR_VERSION = 1
 # sink, stripes) logit boosts are LLM_ALPHA * (1.0, 1.0, 0.75). Found once by
 # bisection so that the 32K-token layer at tau = 0.9 keeps about half of its
 # causal blocks (tests/golden/calibrate_generator.py writes the record).
-LLM_ALPHA = 4.0
+LLM_ALPHA = 10.62
 # Logit boost between equal patch indices of different frames in the video
 # recipe, found the same way on the 64K-token video layer at tau = 0.9.
-VIDEO_BETA = 4.0
+VIDEO_BETA = 111.0
 
 
 @dataclass(frozen=True)
