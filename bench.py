@@ -1,0 +1,223 @@
+"""Benchmark of the RRAttention prefill hot path on one MI355X.
+
+One step = one layer's causal prefill through the C ABI: the round-robin
+pattern search (rr_pattern_search) followed by block-sparse attention over the
+lists it produced (rr_block_sparse_attn), on seeded synthetic bf16 inputs that
+are resident in HBM before timing starts. Default workload: the
+LLaMA-3.1-8B-shaped layer at 131,072 tokens (32 query / 8 KV heads, d = 128,
+B = 128, S = 16, tau = 0.9).
+
+value = effective TFLOP/s of the whole step: F_comp / step time, where F_comp
+counts 4*B*B*d FLOPs per computed off-diagonal block and 2*B*B*d per computed
+diagonal block (the useful FLOPs of the blocks actually computed).
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill attn ms + effective TFLOP/s per layer at 128K; % blocks computed"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+FP32_MATRIX_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def computed_flops(rc: np.ndarray, ci: np.ndarray, B: int, d: int, causal: bool):
+    """(F_comp, blocks computed, diagonal blocks computed) from the block lists."""
+    Hq, nb = rc.shape
+    total = int(rc.sum())
+    if causal:
+        last = ci[np.arange(Hq)[:, None], np.arange(nb)[None, :], np.maximum(rc - 1, 0)]
+        ndiag = int((last == np.arange(nb)[None, :]).sum())
+    else:
+        ndiag = 0
+    f = 4.0 * B * B * d * (total - ndiag) + 2.0 * B * B * d * ndiag
+    return f, total, ndiag
+
+
+def search_logits(w, rows=None) -> int:
+    """Sampled logits the search evaluates (rows: query-block indices, all heads)."""
+    r = w.B // w.S
+    it = range(w.nb - 1) if rows is None else rows
+    n = 0
+    for i in it:
+        if i >= w.nb - 1:
+            continue
+        for a in range(r):
+            s = i * r + a
+            n += (s + 1) if w.causal else w.ns
+    return n * w.Hq
+
+
+def cpu_baseline(w, q, k, v, rc, ci, f_comp, seconds_hint=20.0):
+    """The oracle timed on a bounded sample, extrapolated to the whole step."""
+    import oracle
+    from tests.gpu_cases import sample_rows
+
+    cores = oracle.max_threads()
+    rows_i = sorted({w.nb // 4, w.nb // 2, (3 * w.nb) // 4})
+    mask = np.zeros((w.Hq, w.nb), bool)
+    mask[:, rows_i] = True
+    t0 = time.perf_counter()
+    oracle.search(q, k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=w.dtype == "bf16",
+                  extras=False, row_mask=mask)
+    t_search = time.perf_counter() - t0
+    search_scale = search_logits(w) / max(1, search_logits(w, rows_i))
+
+    srows = sample_rows(w.L, w.Hq, w.B, 504, seed=11)
+    f_sample = 0.0
+    for x, h in srows:
+        i = x // w.B
+        js = ci[h, i, : rc[h, i]]
+        keys = int(sum(min(w.B, x - j * w.B + 1) if (w.causal and j == i) else w.B for j in js))
+        f_sample += 4.0 * w.d * keys
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=srows)
+    t_attn = time.perf_counter() - t0
+    est = t_search * search_scale + t_attn * (f_comp / f_sample)
+    return {
+        "value": f_comp / est / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": ("search rows i in %s for all %d heads (%.2fs, x%.1f to the full search) + "
+                   "attention of %d sampled (token, head) rows on the GPU's block lists (%.2fs, "
+                   "x%.0f by computed FLOPs); extrapolated full step %.0f s"
+                   % (rows_i, w.Hq, t_search, search_scale, len(srows), t_attn, f_comp / f_sample, est)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama8b_L128k")
+    ap.add_argument("--tau", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the operator is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dynamic_block_sparse_rr_amd as rr
+    from synthetic.gen import make_inputs, workload
+
+    w = workload(args.workload)
+    tau = args.tau if args.tau is not None else w.taus[len(w.taus) // 2]
+    log(f"workload {w.name}: L={w.L} Hq={w.Hq} Hkv={w.Hkv} d={w.d} B={w.B} S={w.S} tau={tau}")
+    t0 = time.perf_counter()
+    q, k, v = make_inputs(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    p = rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, tau, w.causal, w.dtype)
+    pre = rr.Prefill(p)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
+        rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
+        ev[s][1].record(stream)
+        rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    search_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (search {search_ms:.3f} ms, attention {attn_ms:.3f} ms)")
+
+    rc = pre.row_count.cpu().numpy()
+    ci = pre.col_idx.cpu().numpy()
+    f_comp, nblocks, ndiag = computed_flops(rc, ci, w.B, w.d, w.causal)
+    causal_blocks = w.Hq * w.nb * (w.nb + 1) // 2 if w.causal else w.Hq * w.nb * w.nb
+    pct = 100.0 * nblocks / causal_blocks
+    attn_tflops = f_comp / (attn_ms * 1e-3) / 1e12
+    value = f_comp / (ms_per_step * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MATRIX_PEAK_TFLOPS
+
+    extra = {}
+    if not args.no_dense:
+        # dense baseline: the same attention kernel with every causal block listed
+        dp = rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, 1.0, w.causal, w.dtype)
+        drc = torch.empty_like(pre.row_count)
+        dci = torch.empty_like(pre.col_idx)
+        rr.rr_pattern_search(dp, qd, kd, drc, dci, None, pre.ws, stream=stream)
+        rr.rr_block_sparse_attn(dp, qd, kd, vd, drc, dci, pre.out, pre.ws, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(2):
+            rr.rr_block_sparse_attn(dp, qd, kd, vd, drc, dci, pre.out, pre.ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / 2
+        f_dense, _, _ = computed_flops(drc.cpu().numpy(), dci.cpu().numpy(), w.B, w.d, w.causal)
+        extra = {"dense_attn_ms": round(dense_ms, 3),
+                 "dense_attn_tflops": round(f_dense / (dense_ms * 1e-3) / 1e12, 1),
+                 "speedup_vs_dense": round(dense_ms / ms_per_step, 3)}
+        del drc, dci
+        log(f"dense attention {dense_ms:.3f} ms")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "B": w.B,
+                   "S": w.S, "tau": tau, "causal": w.causal, "seed": w.seed, "batch": 1},
+        "search_ms": round(search_ms, 3),
+        "attn_ms": round(attn_ms, 3),
+        "search_share": round(search_ms / (search_ms + attn_ms), 4),
+        "blocks_computed_pct": round(pct, 2),
+        "attn_effective_tflops": round(attn_tflops, 1),
+        **extra,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel (timed with the V re-layout pass of the same call)"},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, rc, ci, f_comp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

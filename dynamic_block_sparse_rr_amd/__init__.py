@@ -1,0 +1,185 @@
+"""Python binding of the MI355X (gfx950) RRAttention prefill library.
+
+Thin ctypes marshalling over the C ABI in include/rr_attn.h: every entry point
+has the same name and arguments as there, every step of the computation runs
+in the library's HIP kernels. PyTorch is used only to own device memory and to
+name the stream. There is no CPU fallback: if librr_attn.so is missing, or a
+tensor is not on a GPU, the call raises.
+
+Method: "RRAttention: Dynamic Block Sparse Attention via Per-Head Round-Robin
+Shifts for Long-Context Inference" (abstract, TL;DR, Figure 2 caption).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "Problem", "RRError", "load", "problem", "rr_workspace_bytes", "rr_pattern_search",
+    "rr_block_sparse_attn", "rr_prefill", "rr_status_string", "rr_version", "Prefill",
+    "RR_OK", "RR_ERR_INVALID_ARG", "RR_ERR_UNSUPPORTED", "RR_ERR_WORKSPACE", "RR_ERR_HIP",
+    "RR_BF16", "RR_FP32", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librr_attn.so")
+
+RR_OK, RR_ERR_INVALID_ARG, RR_ERR_UNSUPPORTED, RR_ERR_WORKSPACE, RR_ERR_HIP = 0, 1, 2, 3, 4
+RR_BF16, RR_FP32 = 0, 1
+_DTYPES = {"bf16": RR_BF16, "fp32": RR_FP32}
+
+
+class Problem(ctypes.Structure):
+    """Mirror of rr_problem."""
+
+    _fields_ = [("L", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("S", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    @property
+    def nb(self) -> int:
+        return self.L // self.B
+
+    def __repr__(self):
+        return ("Problem(L=%d, Hq=%d, Hkv=%d, d=%d, S=%d, B=%d, tau=%g, causal=%d, dtype=%d)"
+                % (self.L, self.Hq, self.Hkv, self.d, self.S, self.B, self.tau, self.causal, self.dtype))
+
+
+class RRError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, rr_status_string(status), status))
+
+
+_lib = None
+
+
+def load():
+    """Load librr_attn.so (built by python -m dynamic_block_sparse_rr_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("librr_attn.so is not built; run `python -m dynamic_block_sparse_rr_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(Problem)
+        lib.rr_workspace_bytes.argtypes = [PP]
+        lib.rr_workspace_bytes.restype = ctypes.c_size_t
+        lib.rr_pattern_search.argtypes = [PP, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_pattern_search.restype = ctypes.c_int
+        lib.rr_block_sparse_attn.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_block_sparse_attn.restype = ctypes.c_int
+        lib.rr_prefill.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_prefill.restype = ctypes.c_int
+        lib.rr_status_string.argtypes = [ctypes.c_int]
+        lib.rr_status_string.restype = ctypes.c_char_p
+        lib.rr_version.argtypes = []
+        lib.rr_version.restype = ctypes.c_int32
+        _lib = lib
+    return _lib
+
+
+def problem(L, Hq, Hkv, d, S, B, tau, causal=True, dtype="bf16") -> Problem:
+    dt = _DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    return Problem(int(L), int(Hq), int(Hkv), int(d), int(S), int(B), float(tau), int(bool(causal)), dt)
+
+
+def _ptr(x):
+    """Device address of a GPU tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if not x.is_cuda:
+            raise ValueError("tensor arguments must live on the GPU (got %s)" % x.device)
+        if not x.is_contiguous():
+            raise ValueError("tensor arguments must be contiguous")
+        return x.data_ptr()
+    raise TypeError("expected a GPU tensor, an int device pointer or None, got %r" % type(x))
+
+
+def _nbytes(ws, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    if hasattr(ws, "numel"):
+        return ws.numel() * ws.element_size()
+    return 0
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, status):
+    if status != RR_OK:
+        raise RRError(fn, status)
+
+
+def rr_workspace_bytes(p: Problem) -> int:
+    return int(load().rr_workspace_bytes(ctypes.byref(p)))
+
+
+def rr_pattern_search(p, q, k, row_count, col_idx, block_mass, ws, ws_bytes=None, stream=None):
+    _check("rr_pattern_search", load().rr_pattern_search(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx), _ptr(block_mass),
+        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_block_sparse_attn(p, q, k, v, row_count, col_idx, out, ws, ws_bytes=None, stream=None):
+    _check("rr_block_sparse_attn", load().rr_block_sparse_attn(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_count), _ptr(col_idx), _ptr(out),
+        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_prefill(p, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=None):
+    _check("rr_prefill", load().rr_prefill(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
+        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_status_string(status: int) -> str:
+    return load().rr_status_string(int(status)).decode()
+
+
+def rr_version() -> int:
+    return int(load().rr_version())
+
+
+class Prefill:
+    """Owns the device workspace and outputs for one problem shape (torch allocations)."""
+
+    def __init__(self, p: Problem, device="cuda"):
+        import torch
+
+        self.p = p
+        self.device = torch.device(device)
+        n = rr_workspace_bytes(p)
+        if n == 0:
+            raise RRError("rr_workspace_bytes", RR_ERR_UNSUPPORTED)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        nb = p.nb
+        self.row_count = torch.empty((p.Hq, nb), dtype=torch.int32, device=self.device)
+        self.col_idx = torch.empty((p.Hq, nb, nb), dtype=torch.int32, device=self.device)
+        tdt = torch.bfloat16 if p.dtype == RR_BF16 else torch.float32
+        self.out = torch.empty((p.L, p.Hq, p.d), dtype=tdt, device=self.device)
+
+    def search(self, q, k, block_mass=None):
+        rr_pattern_search(self.p, q, k, self.row_count, self.col_idx, block_mass, self.ws)
+        return self.row_count, self.col_idx
+
+    def attention(self, q, k, v, row_count=None, col_idx=None):
+        rc = self.row_count if row_count is None else row_count
+        ci = self.col_idx if col_idx is None else col_idx
+        rr_block_sparse_attn(self.p, q, k, v, rc, ci, self.out, self.ws)
+        return self.out
+
+    def __call__(self, q, k, v):
+        rr_prefill(self.p, q, k, v, self.out, self.row_count, self.col_idx, self.ws)
+        return self.out, self.row_count, self.col_idx

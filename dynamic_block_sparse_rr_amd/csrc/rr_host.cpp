@@ -1,0 +1,169 @@
+// Host runtime of the C ABI declared in include/rr_attn.h: argument checks,
+// workspace carving and the launch sequence of the two RRAttention stages
+// ("RRAttention: Dynamic Block Sparse Attention via Per-Head Round-Robin
+// Shifts for Long-Context Inference", abstract and Figure 2 caption: search,
+// then sparse attention). Everything is enqueued on the caller's stream; the
+// library allocates nothing and keeps no state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "rr_attn.h"
+#include "rr_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
+  if (!p) return RR_ERR_INVALID_ARG;
+  if (p->L <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0 || p->S <= 0 || p->B <= 0)
+    return RR_ERR_INVALID_ARG;
+  if (p->Hq % p->Hkv != 0) return RR_ERR_INVALID_ARG;
+  if (p->B % p->S != 0 || p->L % p->B != 0) return RR_ERR_INVALID_ARG;
+  if (!(p->tau > 0.0f && p->tau <= 1.0f)) return RR_ERR_INVALID_ARG;  // NaN fails too
+  if (p->causal != 0 && p->causal != 1) return RR_ERR_INVALID_ARG;
+  if (p->dtype != RR_BF16 && p->dtype != RR_FP32) return RR_ERR_INVALID_ARG;
+  if (p->d != 64 && p->d != 128) return RR_ERR_UNSUPPORTED;
+  if (p->B != 64 && p->B != 128) return RR_ERR_UNSUPPORTED;
+  const int r = p->B / p->S;
+  if (!is_pow2(p->S) || r < 2 || r > 32) return RR_ERR_UNSUPPORTED;
+  const int nb = p->L / p->B;
+  if (nb > rr::kMaxSelectBlocks) return RR_ERR_UNSUPPORTED;
+  if ((long long)p->Hq * nb > (1LL << 30)) return RR_ERR_UNSUPPORTED;
+  g->L = p->L;
+  g->Hq = p->Hq;
+  g->Hkv = p->Hkv;
+  g->d = p->d;
+  g->S = p->S;
+  g->B = p->B;
+  g->nb = nb;
+  g->ns = p->L / p->S;
+  g->r = r;
+  g->G = p->Hq / p->Hkv;
+  g->causal = p->causal;
+  g->bf16 = p->dtype == RR_BF16;
+  g->tau = p->tau;
+  return RR_OK;
+}
+
+struct Workspace {
+  size_t kbar, mass, vt, total;  // byte offsets and total size
+};
+
+Workspace layout(const rr::Geometry& g) {
+  const size_t esz = g.bf16 ? 2 : 4;
+  Workspace w;
+  size_t off = 0;
+  w.kbar = off;
+  off += align_up((size_t)g.ns * g.Hkv * g.d * esz);
+  w.mass = off;
+  off += align_up((size_t)g.Hq * g.nb * g.nb * sizeof(float));
+  w.vt = off;
+  if (g.bf16) off += align_up((size_t)g.L * g.Hkv * g.d * esz);
+  w.total = off;
+  return w;
+}
+
+rr_status check_ws(const rr::Geometry& g, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned16(ws) || ws_bytes < layout(g).total) return RR_ERR_WORKSPACE;
+  return RR_OK;
+}
+
+rr_status hip_status(hipError_t e) { return e == hipSuccess ? RR_OK : RR_ERR_HIP; }
+
+rr_status run_search(const rr::Geometry& g, const void* q, const void* k, int32_t* row_count,
+                     int32_t* col_idx, float* block_mass, void* ws, hipStream_t st) {
+  const Workspace w = layout(g);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  void* kbar = base + w.kbar;
+  float* mass = block_mass ? block_mass : reinterpret_cast<float*>(base + w.mass);
+  hipError_t e = rr::launch_pool_keys(g, k, kbar, st);
+  if (e == hipSuccess) e = rr::launch_search(g, q, kbar, mass, st);
+  if (e == hipSuccess) e = rr::launch_select(g, mass, block_mass != nullptr, row_count, col_idx, st);
+  return hip_status(e);
+}
+
+rr_status run_attention(const rr::Geometry& g, const void* q, const void* k, const void* v,
+                        const int32_t* row_count, const int32_t* col_idx, void* out, void* ws,
+                        hipStream_t st) {
+  const Workspace w = layout(g);
+  void* vt = static_cast<uint8_t*>(ws) + w.vt;
+  hipError_t e = hipSuccess;
+  if (g.bf16) e = rr::launch_transpose_v(g, v, vt, st);
+  if (e == hipSuccess) e = rr::launch_attention(g, q, k, v, vt, row_count, col_idx, out, st);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rr_workspace_bytes(const rr_problem* p) {
+  rr::Geometry g;
+  if (make_geometry(p, &g) != RR_OK) return 0;
+  return layout(g).total;
+}
+
+rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k, int32_t* row_count,
+                            int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
+                            void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(row_count) || !aligned16(col_idx))
+    return RR_ERR_INVALID_ARG;
+  if (block_mass && !aligned16(block_mass)) return RR_ERR_INVALID_ARG;
+  if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
+  return run_search(g, q, k, row_count, col_idx, block_mass, ws, static_cast<hipStream_t>(stream));
+}
+
+rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* row_count, const int32_t* col_idx, void* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !v || !row_count || !col_idx || !out) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(row_count) ||
+      !aligned16(col_idx) || !aligned16(out))
+    return RR_ERR_INVALID_ARG;
+  if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
+  return run_attention(g, q, k, v, row_count, col_idx, out, ws, static_cast<hipStream_t>(stream));
+}
+
+rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const void* v, void* out,
+                     int32_t* row_count, int32_t* col_idx, void* ws, size_t ws_bytes, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !v || !out || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(row_count) || !aligned16(col_idx))
+    return RR_ERR_INVALID_ARG;
+  if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = run_search(g, q, k, row_count, col_idx, nullptr, ws, st);
+  if (s != RR_OK) return s;
+  return run_attention(g, q, k, v, row_count, col_idx, out, ws, st);
+}
+
+const char* rr_status_string(rr_status s) {
+  switch (s) {
+    case RR_OK: return "ok";
+    case RR_ERR_INVALID_ARG: return "invalid argument";
+    case RR_ERR_UNSUPPORTED: return "unsupported problem";
+    case RR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RR_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+int32_t rr_version(void) { return 100; }
+
+}  // extern "C"

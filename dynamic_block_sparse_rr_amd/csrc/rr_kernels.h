@@ -1,0 +1,36 @@
+// Internal launch interface between the host runtime (rr_host.cpp) and the
+// gfx950 kernels (search.hip, attn.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rr {
+
+// Geometry shared by the launches of one problem.
+struct Geometry {
+  int L, Hq, Hkv, d, S, B;
+  int nb, ns, r, G;
+  int causal;
+  int bf16;  // 1: bfloat16 tensors, 0: float32
+  float tau;
+};
+
+// Stage 1 launches.
+hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStream_t st);
+hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, float* mass,
+                         hipStream_t st);
+hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
+                         int32_t* col_idx, hipStream_t st);
+
+// Stage 2 launches.
+hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStream_t st);
+hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
+                            const void* vt, const int32_t* row_count, const int32_t* col_idx,
+                            void* out, hipStream_t st);
+
+// Kernel-side limits checked by the host before any launch.
+constexpr int kMaxSelectBlocks = 8192;  // LDS sort capacity of the select kernel (nb): 12 B per key
+
+}  // namespace rr

@@ -1,0 +1,471 @@
+// Stage 1 of RRAttention on gfx950: stride pooling of the keys, the head
+// round-robin sampled scoring with block-mass accumulation, and the adaptive
+// Top-tau block selection with the last query block kept whole.
+//
+// Method: "RRAttention: Dynamic Block Sparse Attention via Per-Head
+// Round-Robin Shifts for Long-Context Inference" -- abstract (head
+// round-robin sampling, stride-level aggregation, O(L^2/S^2), adaptive
+// Top-tau), TL;DR (Top-tau block selection, static protection of the last
+// query block), Figure 2 caption (stride S, block B, three stages).
+//
+// Kernels
+//   pool_keys   K [L][Hkv][d] -> Kbar [L/S][Hkv][d]: float32 sum of the S keys
+//               of a stride in token order, times 1/S (S is a power of two, so
+//               this equals the division), rounded to the input dtype.
+//               HBM stream: reads K once, writes Kbar.
+//   search      one workgroup per (query block i < nb-1, KV head g, chunk of
+//               that group's query heads). Sampled query of head h in stride s
+//               is token s*S + (h mod S). Scores are computed transposed,
+//               Kbar_tile (32 strides x d) * Qs^T (d x 32 sampled queries), on
+//               the 32x32 MFMA so that every lane owns one sampled query and
+//               16 strides of it: softmax statistics need no cross-lane work
+//               except one exchange between the two lane halves. Pass 1 keeps
+//               a running (max, sum) per sampled query, the four waves merge
+//               theirs through LDS in a fixed order; pass 2 recomputes the
+//               scores, forms probabilities and reduces them into key-block
+//               masses with a fixed shuffle tree (deterministic, no atomics).
+//   select      one workgroup per (h, i): bitonic sort of (mass desc, index asc)
+//               keys in LDS, prefix sums of the sorted masses, cut at the first
+//               block whose preceding mass reaches tau * total, and compaction
+//               of the kept blocks into an ascending list.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rr_kernels.h"
+
+namespace rr {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
+  // clang lowers this conversion to v_cvt_pk_bf16_f32: round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ------------------------------------------------------------------ pooling
+
+template <typename T>
+__global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k, T* __restrict__ kbar,
+                                                        int ns, int row_chunks, int S) {
+  // one thread per 16-byte chunk of a pooled row; row_chunks = Hkv * d * sizeof(T) / 16
+  const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (n >= (long long)ns * row_chunks) return;
+  const int t = (int)(n / row_chunks);
+  const int c = (int)(n % row_chunks);
+  const u32x4* src = reinterpret_cast<const u32x4*>(k) + (size_t)t * S * row_chunks + c;
+  const float inv = 1.0f / (float)S;  // exact: S is a power of two
+  u32x4 res;
+  if constexpr (sizeof(T) == 2) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int u = 0; u < S; ++u) {
+      const u32x4 w = src[(size_t)u * row_chunks];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_bits_to_float(w[e] & 0xffffu);
+        acc[2 * e + 1] += bf16_bits_to_float(w[e] >> 16);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      res[e] = float_to_bf16_bits(acc[2 * e] * inv) | (float_to_bf16_bits(acc[2 * e + 1] * inv) << 16);
+  } else {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < S; ++u) {
+      const u32x4 w = src[(size_t)u * row_chunks];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = __float_as_uint(acc[e] * inv);
+  }
+  reinterpret_cast<u32x4*>(kbar)[n] = res;
+}
+
+// ------------------------------------------------------------------ scoring
+
+// 16-byte operand chunk and the 32x32 MFMA accumulate for one chunk.
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+  typedef bf16x8 chunk;
+  static __device__ __forceinline__ f32x16 acc(chunk a, chunk b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  typedef f32x4 chunk;
+  static __device__ __forceinline__ f32x16 acc(chunk a, chunk b, f32x16 c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void merge_max_sum(float& m, float& l, float m2, float l2) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;  // both empty
+  l = l * exp2_approx(m - mm) + l2 * exp2_approx(m2 - mm);
+  m = mm;
+}
+
+// Lane layout of one 32x32 MFMA output (rows = key strides, cols = sampled
+// queries): lane owns column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4.
+__device__ __forceinline__ int out_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
+
+template <typename T, int D, int R>
+__global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, const T* __restrict__ kbar,
+                                                     float* __restrict__ mass, int Hq, int Hkv, int S,
+                                                     int nb, int ns, int causal, int hpc, int nchunk,
+                                                     float cscale) {
+  typedef typename Mfma<T>::chunk chunk_t;
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int NCH = D / (2 * E);   // chunks per lane per row (two lane halves split d)
+  static_assert(R >= 2 && R <= 32 && (R & (R - 1)) == 0, "R = B/S must be a power of two in [2, 32]");
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n32 = lane & 31, half = lane >> 5;
+
+  // work item: long rows first
+  const int chunk = blockIdx.x % nchunk;
+  const int rest = blockIdx.x / nchunk;
+  const int g = rest % Hkv;
+  const int i = (nb - 2) - rest / Hkv;
+  const int G = Hq / Hkv;
+  const int h0 = g * G + chunk * hpc;
+  const int nh = min(hpc, G - chunk * hpc);
+  const int NQ = nh * R;
+  const int NCT = (NQ + 31) >> 5;  // 1 or 2 column tiles of sampled queries
+  const int tcnt = causal ? (i + 1) * R : ns;
+  const int ntile = (tcnt + 31) >> 5;
+
+  // sampled queries (MFMA B operand, kept in registers) and the last visible stride of each
+  chunk_t qf[2][NCH];
+  int lim[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int qi = ct * 32 + n32;
+    if (ct < NCT && qi < NQ) {
+      const int hl = qi / R, a = qi % R;
+      const int h = h0 + hl;
+      const int s = i * R + a;
+      const int pos = s * S + (h % S);  // head round-robin offset
+      const chunk_t* src = reinterpret_cast<const chunk_t*>(q + ((size_t)pos * Hq + h) * D);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qf[ct][c] = src[2 * c + half];
+      lim[ct] = causal ? s : ns - 1;
+    } else {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) qf[ct][c] = chunk_t{};
+      lim[ct] = -1;
+    }
+  }
+
+  // ---- pass 1: running max / sum of exp2(scaled score) per sampled query
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
+  for (int tile = wave; tile < ntile; tile += 4) {
+    const int trow = min(tile * 32 + n32, ns - 1);
+    const chunk_t* src = reinterpret_cast<const chunk_t*>(kbar + ((size_t)trow * Hkv + g) * D);
+    chunk_t kf[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kf[c] = src[2 * c + half];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (ct >= NCT) break;
+      f32x16 acc = {};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc = Mfma<T>::acc(kf[c], qf[ct][c], acc);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tile * 32 + out_row(v, half);
+        acc[v] = (t <= lim[ct]) ? acc[v] * cscale : -INFINITY;
+        tmax = fmaxf(tmax, acc[v]);
+      }
+      if (tmax > -INFINITY) {
+        const float mnew = fmaxf(mrun[ct], tmax);
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += exp2_approx(acc[v] - mnew);
+        lrun[ct] = lrun[ct] * exp2_approx(mrun[ct] - mnew) + sum;
+        mrun[ct] = mnew;
+      }
+    }
+  }
+
+  // merge the two lane halves, then the four waves (fixed order)
+  __shared__ float sm_m[4][64], sm_l[4][64];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float mo = __shfl_xor(mrun[ct], 32);
+    const float lo = __shfl_xor(lrun[ct], 32);
+    merge_max_sum(mrun[ct], lrun[ct], mo, lo);
+    if (half == 0) {
+      sm_m[wave][ct * 32 + n32] = mrun[ct];
+      sm_l[wave][ct * 32 + n32] = lrun[ct];
+    }
+  }
+  __syncthreads();
+  float mu[2], invl[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    float m = sm_m[0][ct * 32 + n32], l = sm_l[0][ct * 32 + n32];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge_max_sum(m, l, sm_m[w][ct * 32 + n32], sm_l[w][ct * 32 + n32]);
+    mu[ct] = m;
+    invl[ct] = l > 0.0f ? 1.0f / l : 0.0f;
+  }
+
+  // ---- pass 2: probabilities summed into key blocks of R strides
+  const float invR = 1.0f / (float)R;  // exact
+  for (int tile = wave; tile < ntile; tile += 4) {
+    const int trow = min(tile * 32 + n32, ns - 1);
+    const chunk_t* src = reinterpret_cast<const chunk_t*>(kbar + ((size_t)trow * Hkv + g) * D);
+    chunk_t kf[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) kf[c] = src[2 * c + half];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (ct >= NCT) break;
+      f32x16 acc = {};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc = Mfma<T>::acc(kf[c], qf[ct][c], acc);
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tile * 32 + out_row(v, half);
+        const float e = exp2_approx(acc[v] * cscale - mu[ct]) * invl[ct];
+        p[v] = (t <= lim[ct]) ? e : 0.0f;
+      }
+      // in-lane sums over the strides of one key block, then across lane halves
+      constexpr int NW = (R == 2) ? 8 : (R == 4 || R == 8) ? 4 : (R == 16) ? 2 : 1;
+      float w[NW];
+      if constexpr (R == 2) {
+#pragma unroll
+        for (int k2 = 0; k2 < 8; ++k2) w[k2] = p[2 * k2] + p[2 * k2 + 1];
+      } else {
+        float w4[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) w4[k4] = ((p[4 * k4] + p[4 * k4 + 1]) + p[4 * k4 + 2]) + p[4 * k4 + 3];
+        if constexpr (R == 4 || R == 8) {
+#pragma unroll
+          for (int k4 = 0; k4 < 4; ++k4) w[k4] = w4[k4];
+        } else if constexpr (R == 16) {
+          w[0] = w4[0] + w4[1];
+          w[1] = w4[2] + w4[3];
+        } else {
+          w[0] = (w4[0] + w4[1]) + (w4[2] + w4[3]);
+        }
+      }
+      if constexpr (R >= 8) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] += __shfl_xor(w[k], 32);
+      }
+      // sum over the R sampled queries of the head (R consecutive lanes)
+#pragma unroll
+      for (int off = 1; off < R; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] += __shfl_xor(w[k], off);
+      }
+      const int qi = ct * 32 + n32;
+      const int hl = qi / R;
+      const bool writer = (qi % R == 0) && hl < nh && (R < 8 || half == 0);
+      if (writer) {
+        float* mrow = mass + ((size_t)(h0 + hl) * nb + i) * nb;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+          int jl;
+          if constexpr (R == 2) jl = 4 * (k >> 1) + 2 * half + (k & 1);
+          else if constexpr (R == 4) jl = 2 * k + half;
+          else jl = k;
+          const int jb = tile * (32 / R) + jl;
+          if (jb < nb && (!causal || jb <= i)) mrow[jb] = w[k] * invR;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ selection
+
+__global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, int zero_fill,
+                                                     int32_t* __restrict__ row_count,
+                                                     int32_t* __restrict__ col_idx, int nb, int causal,
+                                                     float tau) {
+  extern __shared__ uint64_t keys[];  // np2 sort keys, then np2 int flags
+  __shared__ float part[256];
+  __shared__ int ipart[256];
+  __shared__ int cut;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int i = row % nb;
+  const int ncand = causal ? i + 1 : nb;
+  float* mrow = mass + (size_t)row * nb;
+  int32_t* out = col_idx + (size_t)row * nb;
+
+  if (zero_fill) {  // exported masses: non-candidates and the unsearched last row are zero
+    const int from = (i == nb - 1) ? 0 : ncand;
+    for (int j = from + tid; j < nb; j += 256) mrow[j] = 0.0f;
+  }
+  if (i == nb - 1 || tau >= 1.0f) {  // static last-block protection / tau = 1
+    for (int j = tid; j < ncand; j += 256) out[j] = j;
+    if (tid == 0) row_count[row] = ncand;
+    return;
+  }
+
+  int np2 = 1;
+  while (np2 < ncand) np2 <<= 1;
+  int* flags = reinterpret_cast<int*>(keys + np2);
+  for (int j = tid; j < np2; j += 256) {
+    keys[j] = (j < ncand) ? (((uint64_t)(~__float_as_uint(mrow[j])) << 32) | (uint32_t)j) : ~0ull;
+    flags[j] = 0;
+  }
+  if (tid == 0) cut = ncand;
+  __syncthreads();
+
+  // bitonic sort, ascending key = mass descending, block index ascending
+  for (int kk = 2; kk <= np2; kk <<= 1) {
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      for (int idx = tid; idx < (np2 >> 1); idx += 256) {
+        const int a = 2 * idx - (idx & (jj - 1));
+        const int b = a + jj;
+        const uint64_t ka = keys[a], kb = keys[b];
+        const bool up = (a & kk) == 0;
+        if ((ka > kb) == up) {
+          keys[a] = kb;
+          keys[b] = ka;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // prefix sums of the sorted masses: per-thread segments + a fixed-order scan
+  const int seg = (np2 + 255) / 256;
+  const int lo = tid * seg, hi = min(lo + seg, ncand);
+  float s = 0.0f;
+  for (int k = lo; k < hi; ++k) s += __uint_as_float(~(uint32_t)(keys[k] >> 32));
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const float add = (tid >= off) ? part[tid - off] : 0.0f;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  const float total = part[255];
+  const float thr = tau * total;
+  float before = (tid == 0) ? 0.0f : part[tid - 1];
+  for (int k = lo; k < hi; ++k) {
+    if (!(before < thr)) {
+      atomicMin(&cut, k);
+      break;
+    }
+    before += __uint_as_float(~(uint32_t)(keys[k] >> 32));
+  }
+  __syncthreads();
+  const int kept = max(cut, 1);
+  for (int k = tid; k < kept; k += 256) flags[(uint32_t)keys[k]] = 1;
+  __syncthreads();
+
+  // compaction in ascending block order
+  int c = 0;
+  const int jlo = tid * seg, jhi = min(jlo + seg, ncand);
+  for (int j = jlo; j < jhi; ++j) c += flags[j];
+  ipart[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = (tid >= off) ? ipart[tid - off] : 0;
+    __syncthreads();
+    ipart[tid] += add;
+    __syncthreads();
+  }
+  int pos = (tid == 0) ? 0 : ipart[tid - 1];
+  for (int j = jlo; j < jhi; ++j)
+    if (flags[j]) out[pos++] = j;
+  if (tid == 0) row_count[row] = ipart[255];
+}
+
+template <typename T, int D>
+hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, float* mass,
+                           hipStream_t st) {
+  const int hpc = min(g.G, 64 / g.r);
+  const int nchunk = (g.G + hpc - 1) / hpc;
+  const int nrows = g.nb - 1;
+  if (nrows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(nrows * g.Hkv * nchunk));
+  const float cscale = (1.0f / sqrtf((float)g.d)) * 1.4426950408889634f;
+  const T* qq = static_cast<const T*>(q);
+  const T* kk = static_cast<const T*>(kbar);
+#define RR_SEARCH_CASE(RV)                                                                      \
+  case RV:                                                                                      \
+    search_kernel<T, D, RV><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns,   \
+                                                  g.causal, hpc, nchunk, cscale);              \
+    break;
+  switch (g.r) {
+    RR_SEARCH_CASE(2)
+    RR_SEARCH_CASE(4)
+    RR_SEARCH_CASE(8)
+    RR_SEARCH_CASE(16)
+    RR_SEARCH_CASE(32)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef RR_SEARCH_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStream_t st) {
+  const int esz = g.bf16 ? 2 : 4;
+  const int row_chunks = g.Hkv * g.d * esz / 16;
+  const long long n = (long long)g.ns * row_chunks;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (g.bf16)
+    pool_keys_kernel<__bf16><<<grid, 256, 0, st>>>(static_cast<const __bf16*>(k),
+                                                   static_cast<__bf16*>(kbar), g.ns, row_chunks, g.S);
+  else
+    pool_keys_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(k),
+                                                  static_cast<float*>(kbar), g.ns, row_chunks, g.S);
+  return hipGetLastError();
+}
+
+hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, float* mass,
+                         hipStream_t st) {
+  if (g.bf16) return g.d == 128 ? launch_search_r<__bf16, 128>(g, q, kbar, mass, st)
+                                : launch_search_r<__bf16, 64>(g, q, kbar, mass, st);
+  return g.d == 128 ? launch_search_r<float, 128>(g, q, kbar, mass, st)
+                    : launch_search_r<float, 64>(g, q, kbar, mass, st);
+}
+
+hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
+                         int32_t* col_idx, hipStream_t st) {
+  int np2 = 1;
+  while (np2 < g.nb) np2 <<= 1;
+  const size_t lds = (size_t)np2 * (sizeof(uint64_t) + sizeof(int));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  select_kernel<<<dim3((unsigned)(g.Hq * g.nb)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill,
+                                                                 row_count, col_idx, g.nb, g.causal,
+                                                                 g.tau);
+  return hipGetLastError();
+}
+
+}  // namespace rr

@@ -1,0 +1,130 @@
+/*
+ * rr_attn.h -- C ABI of the MI355X (gfx950) RRAttention prefill library.
+ *
+ * The operation is the prefill hot path of "RRAttention: Dynamic Block Sparse
+ * Attention via Per-Head Round-Robin Shifts for Long-Context Inference"
+ * (abstract and TL;DR; the three stages of its Figure 2 caption):
+ *   1. pattern search -- head h samples the query at in-stride offset h mod S
+ *      of every stride of S tokens, scores it against stride-aggregated keys
+ *      (an O(L^2/S^2) estimate), turns each sampled query's scores into a
+ *      softmax, sums it into key blocks of B tokens and averages over the
+ *      query block's samples, then keeps each query-block row's heaviest key
+ *      blocks until their cumulative mass reaches tau (adaptive Top-tau); the
+ *      last query block is statically kept whole;
+ *   2. block-sparse attention -- exact softmax attention of every query over
+ *      the keys of its row's selected blocks (key <= query when causal).
+ *
+ * Conventions shared by every entry point
+ *   - Batch 1, one layer. Q and O are [L][Hq][d], K and V are [L][Hkv][d],
+ *     row-major and contiguous, in the dtype named by the problem (bfloat16
+ *     or float32). Query head h uses KV head h / (Hq / Hkv) (grouped-query
+ *     attention with consecutive grouping).
+ *   - nb = L / B query (and key) blocks. Block lists: row_count is int32
+ *     [Hq][nb], col_idx is int32 [Hq][nb][nb]; row (h, i) selects key blocks
+ *     col_idx[h][i][0 .. row_count[h][i]) in strictly ascending order; the
+ *     remaining entries are unspecified.
+ *   - All tensor arguments are DEVICE pointers, 16-byte aligned. The caller
+ *     owns every buffer; the library allocates and frees nothing and keeps no
+ *     state between calls (it is re-entrant). `stream` is a hipStream_t
+ *     (NULL = the default stream); all work is enqueued asynchronously on it
+ *     and nothing is synchronised: the caller synchronises before reading
+ *     outputs on the host.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; an invalid or unsupported problem returns RR_ERR_INVALID_ARG
+ *     or RR_ERR_UNSUPPORTED and launches nothing. A HIP launch failure
+ *     returns RR_ERR_HIP (outputs are then undefined). Nothing throws across
+ *     the ABI.
+ *
+ * Supported problems: dtype bf16 or fp32; d in {64, 128}; B in {64, 128};
+ * S a power of two with r = B / S in {2, 4, 8, 16, 32}; L a multiple of B;
+ * Hq a multiple of Hkv; 0 < tau <= 1 (tau = 1 keeps every candidate block);
+ * causal 0 or 1.
+ */
+#ifndef RR_ATTN_H
+#define RR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RR_OK = 0,
+  RR_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, tau out of (0, 1], ... */
+  RR_ERR_UNSUPPORTED = 2, /* a valid problem outside the supported set above */
+  RR_ERR_WORKSPACE = 3,   /* ws is NULL or ws_bytes < rr_workspace_bytes(p) */
+  RR_ERR_HIP = 4          /* a HIP runtime or launch error */
+} rr_status;
+
+typedef enum { RR_BF16 = 0, RR_FP32 = 1 } rr_dtype;
+
+typedef struct {
+  int32_t L;      /* tokens */
+  int32_t Hq;     /* query heads */
+  int32_t Hkv;    /* key/value heads, divides Hq */
+  int32_t d;      /* head dimension */
+  int32_t S;      /* stride of the round-robin sampling and key aggregation */
+  int32_t B;      /* block size of the sparse pattern (query and key blocks) */
+  float tau;      /* Top-tau mass threshold, 0 < tau <= 1 */
+  int32_t causal; /* 1: key <= query (at stride, block and token level); 0: none */
+  int32_t dtype;  /* rr_dtype of Q, K, V and O */
+} rr_problem;
+
+/* Bytes of device workspace the calls below need for problem p (0 if p is
+ * invalid or unsupported). One workspace serves every entry point. */
+size_t rr_workspace_bytes(const rr_problem* p);
+
+/*
+ * Stage 1, the round-robin pattern search (abstract: "head round-robin
+ * sampling", "stride-level aggregation", "adaptive Top-tau selection"; TL;DR:
+ * "static protection of the last query block").
+ *   q, k        device inputs, [L][Hq][d] and [L][Hkv][d] in p->dtype.
+ *   row_count   device output int32 [Hq][nb].
+ *   col_idx     device output int32 [Hq][nb][nb] (ascending per row).
+ *   block_mass  optional device output float [Hq][nb][nb] (NULL to skip):
+ *               the block masses m[h][i][j] of the searched rows (zero for
+ *               non-candidate blocks and for the unsearched last row).
+ *   ws          device workspace of ws_bytes >= rr_workspace_bytes(p).
+ * Pooled keys are the stride mean computed in float32 and rounded to the
+ * input dtype; scores use scale 1/sqrt(d); sampled stride s sees key strides
+ * t <= s when causal. Row i < nb-1 keeps the blocks of its (mass descending,
+ * index ascending) order while the mass before a block is < tau * row total.
+ */
+rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
+                            int32_t* row_count, int32_t* col_idx, float* block_mass,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 2, block-sparse attention over given block lists (abstract: "computing
+ * only half of the attention blocks"). The lists may come from
+ * rr_pattern_search or any other source; each row must be non-empty,
+ * ascending, < nb, and (causal) <= its query block index: rows breaking this
+ * give undefined output (the library does not read lists back to the host).
+ *   q, k, v     device inputs in p->dtype; out: device output [L][Hq][d] in p->dtype.
+ *   ws          device workspace (holds a key-major copy of V and the row schedule).
+ * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
+ * p->S and p->tau are not used but must be valid.
+ */
+rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* row_count, const int32_t* col_idx, void* out,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Both stages back to back on one stream: search, then attention over the
+ * lists it produced (row_count / col_idx are outputs, as in stage 1). */
+rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const void* v, void* out,
+                     int32_t* row_count, int32_t* col_idx, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rr_status_string(rr_status s);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t rr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_ATTN_H */

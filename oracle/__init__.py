@@ -65,7 +65,7 @@ def _load():
         lib.rro_round_bf16.restype = ctypes.c_float
         lib.rro_pool.argtypes = [ctypes.POINTER(_Problem), P, P]
         lib.rro_pool.restype = ctypes.c_int
-        lib.rro_search.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, P, P, P,
+        lib.rro_search.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int]
         lib.rro_search.restype = ctypes.c_int
         lib.rro_attention.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P,
@@ -135,8 +135,12 @@ class SearchResult:
 
 
 def search(q, k, *, S: int, B: int, tau: float, causal: bool = True, round_bf16: bool,
-           Hkv: int | None = None, nthreads: int = 0, extras: bool = True) -> SearchResult:
-    """Round-robin pattern search with Top-tau selection (float32 arithmetic)."""
+           nthreads: int = 0, extras: bool = True, row_mask=None) -> SearchResult:
+    """Round-robin pattern search with Top-tau selection (float32 arithmetic).
+
+    row_mask: optional bool [Hq][nb]; only those rows are searched (the others
+    get row_count 0), for spot checks of large layers.
+    """
     q = _f32(q)
     k = _f32(k)
     L, Hq, d = q.shape
@@ -154,9 +158,10 @@ def search(q, k, *, S: int, B: int, tau: float, causal: bool = True, round_bf16:
         kbar = np.zeros((L // S, Hkv, d), np.float32)
     else:
         cminus = cplus = rank = total = kbar = None
+    rm = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8).reshape(Hq, nb)
     rc = _load().rro_search(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx),
                             _ptr(mass), _ptr(cminus), _ptr(cplus), _ptr(rank), _ptr(total),
-                            _ptr(kbar), int(nthreads))
+                            _ptr(kbar), _ptr(rm), int(nthreads))
     if rc:
         raise ValueError("rro_search failed (%d)" % rc)
     return SearchResult(row_count, col_idx, mass, cminus, cplus, rank, total, kbar)

@@ -134,11 +134,13 @@ static int by_mass_desc(const void* a, const void* b) {
  *   cminus, cplus [Hq][nb][nb]  mass before / including block j in the ordering,
  *   rank [Hq][nb][nb]           position of block j in the ordering (-1 if no candidate),
  *   total [Hq][nb]              the row total used for the cut,
- *   kbar [L/S][Hkv][d]          the pooled keys.
+ *   kbar [L/S][Hkv][d]          the pooled keys,
+ *   row_mask [Hq][nb]           compute only rows with a nonzero entry (others
+ *                               get row_count 0 and are otherwise untouched).
  */
 int rro_search(const rro_problem* p, const float* Q, const float* K, int32_t* row_count,
                int32_t* col_idx, float* mass, float* cminus, float* cplus, int32_t* rank,
-               float* total, float* kbar_out, int nthreads) {
+               float* total, float* kbar_out, const uint8_t* row_mask, int nthreads) {
   if (check_problem(p) || !Q || !K || !row_count || !col_idx || !mass) return 1;
   const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, S = p->S, B = p->B;
   const int ns = L / S, nb = L / B, r = B / S, G = Hq / Hkv;
@@ -167,6 +169,10 @@ int rro_search(const rro_problem* p, const float* Q, const float* K, int32_t* ro
         const int off = h % S; /* round-robin offset of head h */
         const int ncand = p->causal ? i + 1 : nb;
         const size_t row = (size_t)h * nb + i;
+        if (row_mask && !row_mask[row]) {
+          row_count[row] = 0;
+          continue;
+        }
         float* m = mass + row * nb;
         for (int j = 0; j < nb; ++j) m[j] = 0.0f;
 

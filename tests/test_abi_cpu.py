@@ -1,0 +1,106 @@
+"""The C-ABI library on the CPU: it loads, exports what include/rr_attn.h
+declares, and rejects invalid arguments on the host before any HIP call (so no
+device is needed). No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_rr_amd as rr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rr.LIB_PATH), reason="librr_attn.so not built")
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "rr_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rr_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
+                            "rr_prefill", "rr_status_string", "rr_version"])
+    lib = ctypes.CDLL(rr.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert rr.rr_version() >= 100
+    for s in range(5):
+        assert rr.rr_status_string(s)
+    assert rr.rr_status_string(99) == "unknown status"
+
+
+def base(**kw):
+    args = dict(L=16384, Hq=32, Hkv=8, d=128, S=16, B=128, tau=0.9, causal=1, dtype=rr.RR_BF16)
+    args.update(kw)
+    return rr.Problem(**args)
+
+
+def test_workspace_bytes():
+    p = base()
+    n = rr.rr_workspace_bytes(p)
+    ns, nb = 16384 // 16, 16384 // 128
+    # pooled keys + block masses + key-major V copy, each 256-byte aligned
+    assert n == ns * 8 * 128 * 2 + 32 * nb * nb * 4 + 16384 * 8 * 128 * 2
+    assert rr.rr_workspace_bytes(base(dtype=rr.RR_FP32)) == ns * 8 * 128 * 4 + 32 * nb * nb * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), rr.RR_ERR_INVALID_ARG),
+    (dict(Hq=30), rr.RR_ERR_INVALID_ARG),           # not a multiple of Hkv
+    (dict(L=1000), rr.RR_ERR_INVALID_ARG),          # not a multiple of B
+    (dict(S=48), rr.RR_ERR_INVALID_ARG),            # B not a multiple of S
+    (dict(tau=0.0), rr.RR_ERR_INVALID_ARG),
+    (dict(tau=1.5), rr.RR_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), rr.RR_ERR_INVALID_ARG),
+    (dict(causal=2), rr.RR_ERR_INVALID_ARG),
+    (dict(dtype=7), rr.RR_ERR_INVALID_ARG),
+    (dict(d=96), rr.RR_ERR_UNSUPPORTED),
+    (dict(B=256, S=16), rr.RR_ERR_UNSUPPORTED),
+    (dict(S=128), rr.RR_ERR_UNSUPPORTED),           # r = 1
+    (dict(S=2), rr.RR_ERR_UNSUPPORTED),             # r = 64
+    (dict(L=128 * 9000), rr.RR_ERR_UNSUPPORTED),    # nb above the select kernel's LDS capacity
+])
+def test_invalid_problems_rejected_on_host(kw, status):
+    p = base(**kw)
+    assert rr.rr_workspace_bytes(p) == 0
+    lib = rr.load()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    rc = lib.rr_pattern_search(ctypes.byref(p), fake, fake, fake, fake, None, fake, 1 << 40, 0)
+    assert rc == status
+    rc = lib.rr_block_sparse_attn(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, 1 << 40, 0)
+    assert rc == status
+    rc = lib.rr_prefill(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, 1 << 40, 0)
+    assert rc == status
+
+
+def test_pointer_and_workspace_checks():
+    p = base()
+    lib = rr.load()
+    ok = 1 << 20
+    need = rr.rr_workspace_bytes(p)
+    # null input
+    assert lib.rr_pattern_search(ctypes.byref(p), None, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    # misaligned input
+    assert lib.rr_block_sparse_attn(ctypes.byref(p), ok + 2, ok, ok, ok, ok, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    # workspace missing / too small / misaligned
+    assert lib.rr_prefill(ctypes.byref(p), ok, ok, ok, ok, ok, ok, None, need, 0) == rr.RR_ERR_WORKSPACE
+    assert lib.rr_prefill(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
+    assert lib.rr_pattern_search(ctypes.byref(p), ok, ok, ok, ok, None, ok + 8, need, 0) == rr.RR_ERR_WORKSPACE
+    assert lib.rr_workspace_bytes(None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    p = base(L=256, Hq=2, Hkv=1)
+    q = torch.zeros((256, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rr.rr_pattern_search(p, q, q, q, q, None, q, stream=0)

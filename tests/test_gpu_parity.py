@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small shapes cover every kernel variant (dtype, d, B, r = B/S, GQA group size,
+one or two sampled-query column tiles, causal or not, a single block, tau = 1)
+and are compared in full. The five workload shapes are compared in full where
+the oracle finishes in seconds, otherwise on sampled rows.
+
+Bars: block lists per tests/checker.py (no 'fail' rows); exported block masses
+within 1e-4 relative + 1e-6 absolute; attention given the same lists within
+max-abs 2e-2 and mean-abs 2e-3 for bf16, 1e-4 / 1e-5 for float32.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic.gen import Workload, workload
+from tests import checker
+from tests.gpu_cases import GpuRun, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN = 2e-2, 2e-3
+F32_MAX, F32_MEAN = 1e-4, 1e-5
+
+
+def tol(w):
+    return (BF16_MAX, BF16_MEAN) if w.dtype == "bf16" else (F32_MAX, F32_MEAN)
+
+
+def g(name, L, Hq, Hkv, d, S, B, dtype, causal=True, kind="gauss", seed=100, n_stripes=8):
+    return Workload(name, L, Hq, Hkv, d, dtype, B, S, (0.9,), seed, kind, n_stripes, causal)
+
+
+SMALL = [
+    (g("llm_g4_r8", 2048, 8, 2, 128, 16, 128, "bf16", kind="llm"), 0.9),
+    (g("llm_g7_two_col_tiles", 1536, 14, 2, 128, 16, 128, "bf16", kind="llm"), 0.9),
+    (g("gauss_r2_d64_b64", 1024, 4, 2, 64, 32, 64, "bf16"), 0.8),
+    (g("gauss_r4", 1024, 8, 4, 128, 32, 128, "bf16"), 0.9),
+    (g("gauss_r16", 2048, 4, 1, 128, 8, 128, "bf16"), 0.9),
+    (g("gauss_r32_d64", 2048, 2, 1, 64, 4, 128, "bf16"), 0.9),
+    (g("gauss_b64_d128", 1024, 4, 1, 128, 8, 64, "bf16"), 0.85),
+    (g("noncausal", 1024, 4, 2, 128, 16, 128, "bf16", causal=False), 0.9),
+    (g("single_block", 128, 2, 1, 128, 16, 128, "bf16"), 0.9),
+    (g("tau_one", 1024, 4, 2, 128, 16, 128, "bf16"), 1.0),
+    (g("fp32_d128", 512, 4, 2, 128, 16, 128, "fp32"), 0.9),
+    (g("fp32_noncausal_b64", 512, 2, 2, 64, 8, 64, "fp32", causal=False), 0.9),
+]
+
+
+def oracle_search(w, tau, q, k, row_mask=None):
+    return oracle.search(q, k, S=w.S, B=w.B, tau=tau, causal=w.causal,
+                         round_bf16=w.dtype == "bf16", row_mask=row_mask)
+
+
+def check_lists(w, tau, rc, ci, orc, rows=None):
+    res = checker.classify(rc, ci, orc, tau, causal=w.causal, rows=rows)
+    say(f"  masks {w.name} tau={tau}: exact={res['exact']} letter={res['letter']} "
+        f"near_tie={res['near_tie']} fail={res['fail']} {res['fail_rows'][:5]}")
+    assert res["fail"] == 0, res["fail_rows"][:10]
+    return res
+
+
+@pytest.mark.parametrize("w,tau", SMALL, ids=[c[0].name for c in SMALL])
+def test_small_shapes_full_parity(w, tau):
+    say(f"case {w.name} tau={tau}")
+    run = GpuRun(w, tau)
+    rc, ci, mass = run.search(export_mass=True)
+    orc = oracle_search(w, tau, run.q, run.k)
+    np.testing.assert_allclose(mass, orc.mass, rtol=1e-4, atol=1e-6)
+    check_lists(w, tau, rc, ci, orc)
+    # attention on the oracle's lists, compared in full
+    want = oracle.attention(run.q, run.k, run.v, orc.row_count, orc.col_idx, B=w.B, causal=w.causal)
+    got = run.attention(orc.row_count, orc.col_idx)
+    mx, mean = checker.output_errors(got, want)
+    say(f"  attention {w.name}: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    tmax, tmean = tol(w)
+    assert mx <= tmax and mean <= tmean
+    # end to end, compared on the GPU's own lists
+    out, rc2, ci2 = run.prefill()
+    np.testing.assert_array_equal(rc2, rc)
+    want2 = oracle.attention(run.q, run.k, run.v, rc2, ci2, B=w.B, causal=w.causal)
+    mx2, mean2 = checker.output_errors(out, want2)
+    assert mx2 <= tmax and mean2 <= tmean
+
+
+def test_tau_one_equals_dense_attention():
+    w = g("dense", 2048, 8, 2, 128, 16, 128, "bf16", kind="llm")
+    run = GpuRun(w, 1.0)
+    out, rc, ci = run.prefill()
+    frc, fci = oracle.full_lists(w.L, w.Hq, w.B)
+    np.testing.assert_array_equal(rc, frc)
+    for h in range(w.Hq):
+        for i in range(w.nb):
+            np.testing.assert_array_equal(ci[h, i, : rc[h, i]], np.arange(i + 1))
+    want = oracle.attention(run.q, run.k, run.v, frc, fci, B=w.B)
+    mx, mean = checker.output_errors(out, want)
+    assert mx <= BF16_MAX and mean <= BF16_MEAN
+
+
+def test_runs_are_bitwise_deterministic():
+    w = g("det", 4096, 8, 2, 128, 16, 128, "bf16", kind="llm")
+    run = GpuRun(w, 0.9)
+    a = run.prefill()
+    b = run.prefill()
+    np.testing.assert_array_equal(a[1], b[1])
+    for h in range(w.Hq):
+        for i in range(w.nb):
+            np.testing.assert_array_equal(a[2][h, i, : a[1][h, i]], b[2][h, i, : b[1][h, i]])
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_query_independence_on_gpu():
+    w = g("qi", 2048, 4, 2, 128, 16, 128, "bf16", kind="llm")
+    run = GpuRun(w, 0.9)
+    rc, ci, _ = run.search(export_mass=False)
+    q2 = run.q.clone()
+    q2[(5 + 1) * w.B:] = -q2[(5 + 1) * w.B:]
+    run2 = GpuRun(w, 0.9, inputs=(q2, run.k, run.v))
+    rc2, ci2, _ = run2.search(export_mass=False)
+    np.testing.assert_array_equal(rc[:, :6], rc2[:, :6])
+    for h in range(w.Hq):
+        for i in range(6):
+            np.testing.assert_array_equal(ci[h, i, : rc[h, i]], ci2[h, i, : rc2[h, i]])
+
+
+# ------------------------------------------------------------------ workload shapes
+
+def _workload_case(name, tau, full_search, n_rows_sample=192, search_rows=None):
+    w = workload(name)
+    say(f"case {name} tau={tau} L={w.L}")
+    run = GpuRun(w, tau)
+    rc, ci, mass = run.search(export_mass=full_search)
+    row_mask = None
+    rows = None
+    if not full_search:
+        row_mask = np.zeros((w.Hq, w.nb), bool)
+        for i in search_rows:
+            row_mask[:, i] = True
+        rows = [(h, i) for h in range(w.Hq) for i in search_rows]
+    orc = oracle_search(w, tau, run.q, run.k, row_mask=row_mask)
+    if full_search:
+        np.testing.assert_allclose(mass, orc.mass, rtol=1e-4, atol=1e-6)
+    res = check_lists(w, tau, rc, ci, orc, rows=rows)
+    keep = rc.sum() / (w.Hq * w.nb * (w.nb + 1) / 2)
+    say(f"  keep fraction {keep:.4f}")
+    # attention on the GPU's lists, compared on sampled rows (full for tiny)
+    out, rc2, ci2 = run.prefill()
+    np.testing.assert_array_equal(rc2, rc)
+    tmax, tmean = tol(w)
+    if w.L <= 1024:
+        want = oracle.attention(run.q, run.k, run.v, rc2, ci2, B=w.B, causal=w.causal)
+        mx, mean = checker.output_errors(out, want)
+    else:
+        srows = sample_rows(w.L, w.Hq, w.B, n_rows_sample, seed=w.seed)
+        want = oracle.attention(run.q, run.k, run.v, rc2, ci2, B=w.B, causal=w.causal, rows=srows)
+        got = out[srows[:, 0], srows[:, 1]]
+        mx, mean = checker.output_errors(got, want)
+    say(f"  attention max-abs {mx:.3e} mean-abs {mean:.3e}")
+    assert mx <= tmax and mean <= tmean
+    return res
+
+
+def test_workload_tiny_fp32_L1k():
+    _workload_case("tiny_fp32_L1k", 0.9, full_search=True)
+
+
+def test_workload_llama8b_L16k():
+    _workload_case("llama8b_L16k", 0.9, full_search=True)
+
+
+@pytest.mark.parametrize("tau", [0.85, 0.9, 0.95])
+def test_workload_llama8b_L32k(tau):
+    _workload_case("llama8b_L32k", tau, full_search=True)
+
+
+def test_workload_video_L64k():
+    w = workload("video_L64k")
+    rows = [0, 1, 2, 63, 64, 200, 255, 256, 400, 503, 504, 505, 509, 510, w.nb - 1]
+    _workload_case("video_L64k", 0.9, full_search=False, search_rows=rows)
+
+
+def test_workload_llama8b_L128k():
+    w = workload("llama8b_L128k")
+    rows = [0, 1, 3, 100, 257, 511, 512, 777, 900, 1000, 1021, 1022, w.nb - 1]
+    _workload_case("llama8b_L128k", 0.9, full_search=False, search_rows=rows)
