@@ -41,9 +41,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float exp2_approx(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats to a packed pair of bfloat16 (round to nearest even), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Position p (0..15) inside a 16-key group of a Vt row holds key key_of_pos(p)
@@ -111,142 +114,241 @@ __device__ __forceinline__ void work_item(int x, int Hq, int Hkv, int nb, int& h
   h = (u % Hkv) * G + hh;
 }
 
+// Shared state of one workgroup of the bf16 kernel.
+template <int D, int BLK>
+struct AttnCtx {
+  static constexpr int NTHR = BLK * 2;               // BLK/32 waves
+  static constexpr int MT = BLK / 32;                // 32-key subtiles
+  static constexpr int NT = D / 32;                  // 32-channel tiles of O
+  static constexpr int DK = D / 16;                  // MFMA k-steps over d
+  static constexpr int TILE = BLK * D * 2;           // bytes of one K or Vt tile
+  static constexpr int NDMA = TILE / (NTHR * 16);    // 16-byte copies per thread per tile
+  static constexpr int KCH = D / 8;                  // 16-byte chunks per K row
+  static constexpr int VCH = BLK / 8;                // 16-byte chunks per Vt row
+  uint8_t* lds_k;
+  uint8_t* lds_v;
+  uint32_t koff, voff;    // this thread's copy source for copy 0, relative to a tile base
+  uint32_t kstep, vstep;  // source distance between consecutive copies (bytes)
+  int kro, vro;          // operand read offsets for chunk 0 (XOR in the chunk index)
+  int wave, qr, half;
+  float cscale;
+};
+
+// Copy n of a thread fetches row (n * RPC + row0) of the tile, RPC = threads
+// per copy / chunks per row. Its swizzled chunk is chunk0 ^ ((n * RPC) mod
+// CH) because row0 < RPC, and chunk bits (16-byte units below the row size)
+// do not overlap row bits, hence the XOR on the offset.
+template <int D, int BLK, int CH>
+__device__ __forceinline__ void copy_tile(const AttnCtx<D, BLK>& cx, const uint8_t* src, uint32_t off,
+                                          uint32_t step, uint8_t* dst) {
+  constexpr int RPC = AttnCtx<D, BLK>::NTHR / CH;
+#pragma unroll
+  for (int n = 0; n < AttnCtx<D, BLK>::NDMA; ++n)
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>((src + (size_t)(n * step)) + (off ^ (((n * RPC) & (CH - 1)) << 4))),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(
+            reinterpret_cast<uintptr_t>(dst + (n * AttnCtx<D, BLK>::NTHR + cx.wave * 64) * 16)),
+        16, 0, 0);
+}
+
+// One key block. On entry K (and possibly V) copies of this block are in
+// flight; next_k / next_v are the sources of the following block (null at the
+// end). diag: the key block is the query block itself under the causal flag,
+// keys after the query are masked.
+template <int D, int BLK>
+__device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x8 (&qf)[D / 16],
+                                          f32x16 (&oacc)[D / 32], float& mrow, float& lrow,
+                                          const uint8_t* next_k, const uint8_t* next_v, bool diag) {
+  constexpr int MT = AttnCtx<D, BLK>::MT;
+  constexpr int NT = AttnCtx<D, BLK>::NT;
+  constexpr int DK = AttnCtx<D, BLK>::DK;
+
+  constexpr int NDMA = AttnCtx<D, BLK>::NDMA;
+  // K of this block has landed (its V may still be in flight)
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+  // S^T = K Q^T: rows are keys, the lane's column is its query
+  // operand reads run LA steps ahead of the MFMAs through a register ring
+  constexpr int LA = 4;
+  constexpr int NQK = MT * DK;
+  auto kread = [&](int k) {
+    return *reinterpret_cast<const bf16x8*>(cx.lds_k + (k / DK) * 32 * D * 2 + (cx.kro ^ ((k % DK) << 5)));
+  };
+  f32x16 sacc[MT];
+  bf16x8 ring[LA];
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = kread(k);
+#pragma unroll
+  for (int k = 0; k < NQK; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NQK) ring[k % LA] = kread(k + LA);
+    const int mt = k / DK, cc = k % DK;
+    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc ? sacc[mt] : f32x16{}, 0, 0, 0);
+  }
+  // every wave is done with the K buffer: the next block's K may land in it
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (next_k) copy_tile<D, BLK, AttnCtx<D, BLK>::KCH>(cx, next_k, cx.koff, cx.kstep, cx.lds_k);
+
+  // online softmax in base 2 (scale folded into cscale)
+  if (diag) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
+        if (key > cx.qr) sacc[mt][v] = -INFINITY;
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float mnew = fmaxf(mrow, tmax * cx.cscale);
+  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
+    const float alpha = exp2_approx(mrow - mnew);
+    lrow *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+  }
+  mrow = mnew;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 pf[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
+        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
+        ps[e] += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[mt][p2] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+  // V of this block has landed (the next block's K may still be in flight)
+  if (next_k)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  // O^T += Vt P^T, operand reads again LA steps ahead
+  constexpr int NPV = NT * MT * 2;
+  auto vread = [&](int k) {
+    const int t = k / (MT * 2), r = k % (MT * 2);
+    return *reinterpret_cast<const bf16x8*>(cx.lds_v + t * 32 * BLK * 2 + (cx.vro ^ (((r >> 1) * 4 + 2 * (r & 1)) << 4)));
+  };
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = vread(k);
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NPV) ring[k % LA] = vread(k + LA);
+    const int t = k / (MT * 2), r = k % (MT * 2);
+    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r >> 1][r & 1], oacc[t], 0, 0, 0);
+  }
+  // every wave is done with the V buffer: the next block's V may land in it
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (next_v) copy_tile<D, BLK, AttnCtx<D, BLK>::VCH>(cx, next_v, cx.voff, cx.vstep, cx.lds_v);
+}
+
 template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
     int Hq, int Hkv, int nb, int causal, float cscale) {
-  constexpr int NTHR = BLK * 2;  // BLK/32 waves
-  constexpr int KCH = D / 8;     // 16-byte chunks per K row
-  constexpr int VCH = BLK / 8;   // 16-byte chunks per Vt row
-  constexpr int MT = BLK / 32;   // 32-key tiles
-  constexpr int NT = D / 32;     // 32-channel tiles of O
-  constexpr int DK = D / 16;     // MFMA k-steps over d
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[BLK * D * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[D * BLK * 2];
+  typedef AttnCtx<D, BLK> C;
+  constexpr int KCH = C::KCH;
+  constexpr int VCH = C::VCH;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[C::TILE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n32 = lane & 31, half = lane >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  C cx;
+  cx.lds_k = lds_k;
+  cx.lds_v = lds_v;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31;
+  cx.half = lane >> 5;
+  cx.cscale = cscale;
   int h, i;
   work_item(blockIdx.x, Hq, Hkv, nb, h, i);
   const int G = Hq / Hkv;
   const int g = h / G;
-  const int qr = wave * 32 + n32;  // query row inside the block
-  const int x = i * BLK + qr;
+  cx.qr = cx.wave * 32 + n32;  // query row inside the block
+  const int x = i * BLK + cx.qr;
 
-  bf16x8 qf[DK];
+  // Tiles live in LDS as rows of 16-byte chunks, chunk c of row r stored at
+  // position c ^ (r mod chunks-per-row), so the 32 rows one MFMA operand read
+  // touches fall in distinct banks. Copies write LDS linearly (lane l of a
+  // wave's copy lands at 16*l), so each thread fetches the global chunk that
+  // belongs at its position: a base offset, a fixed step per copy, and a
+  // per-copy XOR of the chunk (see copy_tile).
+  static_assert(C::NTHR % KCH == 0 && C::NTHR % VCH == 0, "copy rows must advance evenly");
+  {
+    const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
+    cx.koff = (kr * Hkv * D + kc * 8) * 2;
+    cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
+    const int vr = tid / VCH, vc = (tid % VCH) ^ (vr & (VCH - 1));
+    cx.voff = (vr * BLK + vc * 8) * 2;
+    cx.vstep = (C::NTHR / VCH) * BLK * 2;
+  }
+  // An operand read of chunk c in a row r = 32*m + n32 is at r*rowbytes +
+  // 16*(c ^ (n32 mod chunks)); with c = 2*cc + half that is kro ^ (32*cc).
+  cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
+  cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
+
+  bf16x8 qf[C::DK];
   {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
 #pragma unroll
-    for (int c = 0; c < DK; ++c) qf[c] = src[2 * c + half];
+    for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
   }
-
-  f32x16 oacc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) oacc[t] = f32x16{};
-  float mrow = -INFINITY, lrow = 0.0f;
 
   const size_t row = (size_t)h * nb + i;
   const int cnt = min(max(row_count[row], 0), nb);
   const int32_t* lst = col_idx + row * nb;
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k);
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(vt);
+  const int jmax = causal ? i : nb - 1;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
+  const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
 
-  for (int c = 0; c < cnt; ++c) {
-    const int j = min(max(lst[c], 0), nb - 1);
-    if (causal && j > i) continue;
-    __syncthreads();  // previous tile fully consumed
+  f32x16 oacc[C::NT];
 #pragma unroll
-    for (int it = 0; it < (BLK * KCH) / NTHR; ++it) {
-      const int n = threadIdx.x + it * NTHR;
-      const int r = n / KCH, ch = n % KCH;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(kbase + (((size_t)(j * BLK + r) * Hkv + g) * D + ch * 8) * 2);
-      *reinterpret_cast<u32x4*>(lds_k + r * D * 2 + ((ch ^ (r & (KCH - 1))) << 4)) = w;
-    }
-#pragma unroll
-    for (int it = 0; it < (D * VCH) / NTHR; ++it) {
-      const int n = threadIdx.x + it * NTHR;
-      const int r = n / VCH, ch = n % VCH;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(vbase + ((((size_t)g * nb + j) * D + r) * BLK + ch * 8) * 2);
-      *reinterpret_cast<u32x4*>(lds_v + r * BLK * 2 + ((ch ^ (r & (VCH - 1))) << 4)) = w;
-    }
-    __syncthreads();
+  for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
+  float mrow = -INFINITY, lrow = 0.0f;
 
-    // S^T = K Q^T
-    f32x16 sacc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      sacc[mt] = f32x16{};
-      const int r = mt * 32 + n32;
-#pragma unroll
-      for (int cc = 0; cc < DK; ++cc) {
-        const int ch = 2 * cc + half;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_k + r * D * 2 + ((ch ^ (r & (KCH - 1))) << 4));
-        sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sacc[mt], 0, 0, 0);
-      }
-    }
-
-    // online softmax in base 2
-    const bool diag = causal && (j == i);
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (diag && key > qr) sacc[mt][v] = -INFINITY;
-        tmax = fmaxf(tmax, sacc[mt][v]);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(mrow, tmax * cscale);
-    const float alpha = exp2_approx(mrow - mnew);
-    float psum = 0.0f;
-    bf16x8 pf[MT][2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cscale, -mnew));
-          const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cscale, -mnew));
-          psum += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
-        }
-        pf[mt][p2] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-    lrow = lrow * alpha + psum;
-    mrow = mnew;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-
-    // O^T += Vt P^T
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r = t * 32 + n32;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-          const int ch = mt * 4 + 2 * p2 + half;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds_v + r * BLK * 2 + ((ch ^ (r & (VCH - 1))) << 4));
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mt][p2], oacc[t], 0, 0, 0);
-        }
-      }
-    }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // queries are in registers
+  int j = cnt > 0 ? min(max(lst[0], 0), jmax) : 0;
+  if (cnt > 0) {
+    copy_tile<D, BLK, KCH>(cx, kg + j * kstride, cx.koff, cx.kstep, lds_k);
+    copy_tile<D, BLK, VCH>(cx, vg + (size_t)j * C::TILE, cx.voff, cx.vstep, lds_v);
   }
+  // Lists are ascending, so under the causal flag only the last entry can be
+  // the diagonal block: the loop never masks, the peeled last entry may.
+  for (int c = 0; c + 1 < cnt; ++c) {
+    const int jn = min(max(lst[c + 1], 0), jmax);
+    attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, kg + jn * kstride, vg + (size_t)jn * C::TILE, false);
+    j = jn;
+  }
+  if (cnt > 0) attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, nullptr, nullptr, causal && j == i);
 
   const float ltot = lrow + __shfl_xor(lrow, 32);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int t = 0; t < C::NT; ++t) {
 #pragma unroll
     for (int v4 = 0; v4 < 4; ++v4) {
-      const int e = t * 32 + 8 * v4 + 4 * half;
+      const int e = t * 32 + 8 * v4 + 4 * cx.half;
       u32x2 w;
       w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
       w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
