@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
+                         "scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -128,6 +131,12 @@ def main():
     q, k, v = make_inputs(w)
     log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     p = rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, tau, w.causal, w.dtype)
     pre = rr.Prefill(p)
     stream = torch.cuda.current_stream()

@@ -28,6 +28,7 @@
 // online softmax in registers).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "rr_kernels.h"
 
@@ -357,6 +358,287 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
+// ------------------------------------------------------------------ bf16 attention, head pairs
+
+// Two query heads of one KV head share a workgroup of 2 * B/32 waves (two per
+// SIMD, 32 queries each). The workgroup walks the merged, ascending block
+// list of both heads: each K/Vt tile is copied once for both, and a wave
+// computes only the blocks its own head selected. K and Vt are
+// double-buffered (four tiles, 128 KiB at B = d = 128): the copy of the next
+// block is issued right after the one barrier per block and has the whole
+// block's compute to land.
+template <int D, int BLK>
+struct PairCtx {
+  static constexpr int WPH = BLK / 32;               // waves per head
+  static constexpr int NTHR = 2 * WPH * 64;          // threads per workgroup
+  static constexpr int MT = BLK / 32;                // 32-key subtiles
+  static constexpr int NT = D / 32;                  // 32-channel tiles of O
+  static constexpr int DK = D / 16;                  // MFMA k-steps over d
+  static constexpr int TILE = BLK * D * 2;           // bytes of one K or Vt tile
+  static constexpr int NDMA = TILE / (NTHR * 16);    // 16-byte copies per thread per tile
+  static constexpr int KCH = D / 8;                  // 16-byte chunks per K row
+  static constexpr int VCH = BLK / 8;                // 16-byte chunks per Vt row
+  uint32_t koff, voff;    // this thread's copy source for copy 0, relative to a tile base
+  uint32_t kstep, vstep;  // source distance between consecutive copies (bytes)
+  int kro, vro;           // operand read offsets for chunk 0 (XOR in the chunk index)
+  int wave, qr, half;
+  float cscale;
+};
+
+template <int D, int BLK, int CH>
+__device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, const uint8_t* src, uint32_t off,
+                                          uint32_t step, uint8_t* dst) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int RPC = C::NTHR / CH;
+#pragma unroll
+  for (int n = 0; n < C::NDMA; ++n)
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>((src + (size_t)(n * step)) + (off ^ (((n * RPC) & (CH - 1)) << 4))),
+        reinterpret_cast<__attribute__((address_space(3))) void*>(
+            reinterpret_cast<uintptr_t>(dst + (n * C::NTHR + cx.wave * 64) * 16)),
+        16, 0, 0);
+}
+
+// One key block for one wave, operands already in LDS (no barriers inside).
+template <int D, int BLK, bool DIAG>
+__device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8_t* lds_k, const uint8_t* lds_v,
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& mrow,
+                                          float& lrow) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int MT = C::MT;
+  constexpr int NT = C::NT;
+  constexpr int DK = C::DK;
+  constexpr int LA = 4;  // operand reads run LA MFMAs ahead through a register ring
+  constexpr int NQK = MT * DK;
+  auto kread = [&](int k) {
+    return *reinterpret_cast<const bf16x8*>(lds_k + (k / DK) * 32 * D * 2 + (cx.kro ^ ((k % DK) << 5)));
+  };
+  f32x16 sacc[MT];
+  bf16x8 ring[LA];
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = kread(k);
+#pragma unroll
+  for (int k = 0; k < NQK; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NQK) ring[k % LA] = kread(k + LA);
+    const int mt = k / DK, cc = k % DK;
+    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc ? sacc[mt] : f32x16{}, 0, 0, 0);
+  }
+  if (DIAG) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
+        if (key > cx.qr) sacc[mt][v] = -INFINITY;
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float mnew = fmaxf(mrow, tmax * cx.cscale);
+  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
+    const float alpha = exp2_approx(mrow - mnew);
+    lrow *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+  }
+  mrow = mnew;
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 pf[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
+        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
+        ps[e] += p0 + p1;
+        w[e] = pack_bf16x2(p0, p1);
+      }
+      pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+    }
+  }
+  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  // O^T += Vt P^T
+  constexpr int NPV = NT * MT * 2;
+  auto vread = [&](int k) {
+    const int t = k / (MT * 2), r = k % (MT * 2);
+    return *reinterpret_cast<const bf16x8*>(lds_v + t * 32 * BLK * 2 + (cx.vro ^ (((r >> 1) * 4 + 2 * (r & 1)) << 4)));
+  };
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = vread(k);
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NPV) ring[k % LA] = vread(k + LA);
+    const int t = k / (MT * 2), r = k % (MT * 2);
+    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r >> 1][r & 1], oacc[t], 0, 0, 0);
+  }
+}
+
+// Launch index -> (KV head g, query block i, head pair p): query blocks in
+// decreasing order, the pairs of one (g, i) on one XCD in consecutive slots.
+__device__ __forceinline__ void pair_item(int x, int Hkv, int nb, int npairs, int& g, int& i, int& p) {
+  const int nunits = Hkv * nb;
+  int u;
+  if ((nunits & 7) == 0) {
+    const int xcd = x & 7, t = x >> 3;
+    p = t % npairs;
+    u = (t / npairs) * 8 + xcd;
+  } else {
+    u = x / npairs;
+    p = x % npairs;
+  }
+  i = nb - 1 - u / Hkv;
+  g = u % Hkv;
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pair_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
+    const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
+    int Hq, int Hkv, int nb, int causal, float cscale) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int KCH = C::KCH;
+  constexpr int VCH = C::VCH;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[2][C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  C cx;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = cx.wave / C::WPH;  // which head of the pair this wave serves
+  const int n32 = lane & 31;
+  cx.half = lane >> 5;
+  cx.qr = (cx.wave % C::WPH) * 32 + n32;
+  cx.cscale = cscale;
+  const int G = Hq / Hkv;
+  const int npairs = (G + 1) / 2;
+  int g, i, p;
+  pair_item(blockIdx.x, Hkv, nb, npairs, g, i, p);
+  const int hA = g * G + 2 * p;
+  const bool hasB = 2 * p + 1 < G;
+  const int hB = hA + 1;
+  const int h = slot ? hB : hA;
+  const bool active = slot == 0 || hasB;  // a lone last head leaves slot 1 idle
+  const int x = i * BLK + cx.qr;
+
+  static_assert(C::NTHR % KCH == 0 && C::NTHR % VCH == 0, "copy rows must advance evenly");
+  {
+    const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
+    cx.koff = (kr * Hkv * D + kc * 8) * 2;
+    cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
+    const int vr = tid / VCH, vc = (tid % VCH) ^ (vr & (VCH - 1));
+    cx.voff = (vr * BLK + vc * 8) * 2;
+    cx.vstep = (C::NTHR / VCH) * BLK * 2;
+  }
+  cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
+  cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
+
+  bf16x8 qf[C::DK];
+  if (active) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
+  }
+
+  // the two block lists, merged on the fly (all values wave-uniform)
+  const int jlast = causal ? i : nb - 1;  // largest admissible key block
+  const int jdiag = causal ? i : nb;      // the masked block, if any
+  const size_t rowA = (size_t)hA * nb + i, rowB = (size_t)hB * nb + i;
+  const int cntA = min(max(row_count[rowA], 0), nb);
+  const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
+  const int32_t* la = col_idx + rowA * nb;
+  const int32_t* lb = col_idx + rowB * nb;
+  constexpr int kNone = 1 << 30;
+  int ia = 0, ib = 0;
+  int ja = cntA > 0 ? min(max(la[0], 0), jlast) : kNone;
+  int jb = cntB > 0 ? min(max(lb[0], 0), jlast) : kNone;
+
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
+  const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
+
+  f32x16 oacc[C::NT];
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
+  float mrow = -INFINITY, lrow = 0.0f;
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // queries are in registers
+  int j = min(ja, jb);
+  int stage = 0;
+  if (j <= jlast) {
+    pair_copy<D, BLK, KCH>(cx, kg + j * kstride, cx.koff, cx.kstep, lds_k[0]);
+    pair_copy<D, BLK, VCH>(cx, vg + (size_t)j * C::TILE, cx.voff, cx.vstep, lds_v[0]);
+  }
+  // every block before the diagonal; the diagonal, last in both lists, after
+  while (j < jdiag) {
+    const bool selA = ja == j, selB = jb == j;
+    if (selA) {
+      ++ia;
+      ja = ia < cntA ? min(max(la[ia], 0), jlast) : kNone;
+    }
+    if (selB) {
+      ++ib;
+      jb = ib < cntB ? min(max(lb[ib], 0), jlast) : kNone;
+    }
+    const int jn = min(ja, jb);
+    // this block's tiles have landed everywhere, and every wave is done with
+    // the other stage, which the next block's copy now reuses
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (jn <= jlast) {
+      pair_copy<D, BLK, KCH>(cx, kg + jn * kstride, cx.koff, cx.kstep, lds_k[stage ^ 1]);
+      pair_copy<D, BLK, VCH>(cx, vg + (size_t)jn * C::TILE, cx.voff, cx.vstep, lds_v[stage ^ 1]);
+    }
+    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, lds_k[stage], lds_v[stage], qf, oacc, mrow, lrow);
+    stage ^= 1;
+    j = jn;
+  }
+  if (j == jdiag) {
+    const bool selA = ja == j, selB = jb == j;
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (slot ? selB : selA) pair_tile<D, BLK, true>(cx, lds_k[stage], lds_v[stage], qf, oacc, mrow, lrow);
+  }
+
+  if (!active) return;
+  const float ltot = lrow + __shfl_xor(lrow, 32);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int e = t * 32 + 8 * v4 + 4 * cx.half;
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
+      w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(dst + e) = w;
+    }
+  }
+}
+
+// Variant switch for measurement: RR_ATTN_PAIR=0 selects the one-head-per-workgroup kernel.
+bool attn_pair_enabled() {
+  static const bool on = [] {
+    const char* e = getenv("RR_ATTN_PAIR");
+    return !(e && e[0] == '0');
+  }();
+  return on;
+}
+
 // ------------------------------------------------------------------ fp32 attention
 
 template <int D, int BLK>
@@ -446,6 +728,17 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
                                                       g.Hkv, g.nb, g.causal, cscale);            \
     return hipGetLastError();                                                                     \
   }
+    const int G = g.Hq / g.Hkv;
+    if (g.B == 128 && G >= 2 && attn_pair_enabled()) {
+      const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
+      if (g.d == 128)
+        attn_bf16_pair_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                              g.nb, g.causal, cscale);
+      else
+        attn_bf16_pair_kernel<64, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                             g.nb, g.causal, cscale);
+      return hipGetLastError();
+    }
     RR_ATTN_CASE(128, 128)
     RR_ATTN_CASE(128, 64)
     RR_ATTN_CASE(64, 128)
