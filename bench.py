@@ -36,6 +36,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload_name: str, tau: float):
+    """HBM bytes per attention call from the committed counter record, or None.
+
+    The record (profiles/attn_bf16_<workload>_traffic.json) holds FETCH_SIZE and
+    WRITE_SIZE of the attention kernel scaled against a plain 1 GiB copy, and the
+    sha256 of the kernel source they were taken on; a changed kernel reports None.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "attn_bf16_%s_traffic.json" % workload_name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "csrc", "attn.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    if abs(float(rec.get("tau", -1)) - tau) > 1e-9:
+        return None
+    return float(rec["traffic_bytes"]), float(rec["algorithmic_bytes"])
+
+
 def computed_flops(rc: np.ndarray, ci: np.ndarray, B: int, d: int, causal: bool):
     """(F_comp, blocks computed, diagonal blocks computed) from the block lists."""
     Hq, nb = rc.shape
@@ -220,8 +241,13 @@ def main():
         **extra,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel (timed with the V re-layout pass of the same call)"},
+                     "kernel": "bf16 block-sparse attention (timed with the V re-layout pass of the same call)"},
     }
+    tr = measured_traffic(w.name, tau)
+    if tr is not None:
+        line["roofline"]["traffic"] = tr[0]
+        line["roofline"]["traffic_unit"] = "bytes per attention call (HBM, FETCH_SIZE + WRITE_SIZE)"
+        line["roofline"]["algorithmic_bytes"] = tr[1]
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, rc, ci, f_comp)

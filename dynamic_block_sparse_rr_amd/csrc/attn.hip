@@ -450,6 +450,9 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
     for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
   }
   mrow = mnew;
+  // P in bf16 (B operand of O^T += Vt P^T); the row sum adds exactly the
+  // rounded values the MFMA multiplies, two at a time
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 pf[MT][2];
 #pragma unroll
@@ -461,8 +464,8 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
       for (int e = 0; e < 4; ++e) {
         const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
         const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
-        ps[e] += p0 + p1;
         w[e] = pack_bf16x2(p0, p1);
+        ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
       }
       pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
     }
