@@ -367,6 +367,15 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
 // double-buffered (four tiles, 128 KiB at B = d = 128): the copy of the next
 // block is issued right after the one barrier per block and has the whole
 // block's compute to land.
+//
+// The copies are buffer loads with an LDS destination, and every stage of
+// the double buffer is an LDS object of its own with the stage fixed at
+// compile time (the block loop is unrolled by two). Both matter to the
+// compiler's wait-count insertion: a flat/global LDS copy in flight makes it
+// wait for all LDS traffic (lgkmcnt(0)) before every operand read, and a copy
+// into the same LDS object as the operands makes it wait for the copy itself
+// (vmcnt(0)) before the first read. With both, the operand reads of block j
+// run while the copy of block j + 1 is still in flight.
 template <int D, int BLK>
 struct PairCtx {
   static constexpr int WPH = BLK / 32;               // waves per head
@@ -385,18 +394,27 @@ struct PairCtx {
   float cscale;
 };
 
+// One tile: NDMA buffer loads of 16 bytes per lane straight into LDS (lane l
+// of a wave lands at 16*l past the wave's slot), from a descriptor based at
+// the tile's first byte.
 template <int D, int BLK, int CH>
-__device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, const uint8_t* src, uint32_t off,
+__device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, __amdgpu_buffer_rsrc_t rsrc, uint32_t off,
                                           uint32_t step, uint8_t* dst) {
   typedef PairCtx<D, BLK> C;
   constexpr int RPC = C::NTHR / CH;
 #pragma unroll
   for (int n = 0; n < C::NDMA; ++n)
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>((src + (size_t)(n * step)) + (off ^ (((n * RPC) & (CH - 1)) << 4))),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc,
         reinterpret_cast<__attribute__((address_space(3))) void*>(
             reinterpret_cast<uintptr_t>(dst + (n * C::NTHR + cx.wave * 64) * 16)),
-        16, 0, 0);
+        16, (int)(n * step + (off ^ (((n * RPC) & (CH - 1)) << 4))), 0, 0, 0);
+}
+
+// Buffer descriptor over `bytes` bytes from p (raw addressing, no stride;
+// reads beyond the range return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, (int)bytes, 0x00020000);
 }
 
 // One key block for one wave, operands already in LDS (no barriers inside).
@@ -424,6 +442,16 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
     const int mt = k / DK, cc = k % DK;
     sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc ? sacc[mt] : f32x16{}, 0, 0, 0);
   }
+  // issue order: LA operand reads, then alternately one MFMA and the read LA
+  // steps ahead (left to itself the scheduler keeps only one or two reads in
+  // flight)
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+  for (int k = 0; k < NQK - LA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
   if (DIAG) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -486,6 +514,13 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
     const int t = k / (MT * 2), r = k % (MT * 2);
     oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r >> 1][r & 1], oacc[t], 0, 0, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 1);
+#pragma unroll
+  for (int k = 0; k < NPV - LA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
 }
 
 // Launch index -> (KV head g, query block i, head pair p): query blocks in
@@ -513,8 +548,10 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   typedef PairCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   constexpr int VCH = C::VCH;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k[2][C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[2][C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -580,15 +617,22 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
   float mrow = -INFINITY, lrow = 0.0f;
 
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // queries are in registers
+  // vmcnt(0) lgkmcnt(0) through the builtin, so the compiler's wait
+  // bookkeeping knows the counters are clear
+  constexpr int kWaitAll = 0x0070;
+  __builtin_amdgcn_s_waitcnt(kWaitAll);  // queries are in registers
+  // K rows of block j start at kg + j*kstride (row pitch Hkv*d*2 bytes); its Vt
+  // tile is the contiguous TILE bytes at vg + j*TILE
+  const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+  auto copy_block = [&](int jb_, uint8_t* kdst, uint8_t* vdst) {
+    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jb_ * kstride, kbytes), cx.koff, cx.kstep, kdst);
+    pair_copy<D, BLK, VCH>(cx, tile_rsrc(vg + (size_t)jb_ * C::TILE, C::TILE), cx.voff, cx.vstep, vdst);
+  };
   int j = min(ja, jb);
-  int stage = 0;
-  if (j <= jlast) {
-    pair_copy<D, BLK, KCH>(cx, kg + j * kstride, cx.koff, cx.kstep, lds_k[0]);
-    pair_copy<D, BLK, VCH>(cx, vg + (size_t)j * C::TILE, cx.voff, cx.vstep, lds_v[0]);
-  }
-  // every block before the diagonal; the diagonal, last in both lists, after
-  while (j < jdiag) {
+  if (j <= jlast) copy_block(j, lds_k0, lds_v0);
+  // One block j whose tiles are in (kc, vc); the next block's copy goes to
+  // (kn, vn).
+  auto step = [&](const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
     const bool selA = ja == j, selB = jb == j;
     if (selA) {
       ++ia;
@@ -601,19 +645,33 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     const int jn = min(ja, jb);
     // this block's tiles have landed everywhere, and every wave is done with
     // the other stage, which the next block's copy now reuses
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (jn <= jlast) {
-      pair_copy<D, BLK, KCH>(cx, kg + jn * kstride, cx.koff, cx.kstep, lds_k[stage ^ 1]);
-      pair_copy<D, BLK, VCH>(cx, vg + (size_t)jn * C::TILE, cx.voff, cx.vstep, lds_v[stage ^ 1]);
-    }
-    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, lds_k[stage], lds_v[stage], qf, oacc, mrow, lrow);
-    stage ^= 1;
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+    if (jn <= jlast) copy_block(jn, kn, vn);
+    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, kc, vc, qf, oacc, mrow, lrow);
     j = jn;
+  };
+  // every block before the diagonal, two per trip so that each stage's LDS
+  // objects are known at compile time; the diagonal, last in both lists, after
+  bool odd = false;
+  while (j < jdiag) {
+    step(lds_k0, lds_v0, lds_k1, lds_v1);
+    if (j >= jdiag) {
+      odd = true;
+      break;
+    }
+    step(lds_k1, lds_v1, lds_k0, lds_v0);
   }
   if (j == jdiag) {
     const bool selA = ja == j, selB = jb == j;
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (slot ? selB : selA) pair_tile<D, BLK, true>(cx, lds_k[stage], lds_v[stage], qf, oacc, mrow, lrow);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+    if (slot ? selB : selA) {
+      if (odd)
+        pair_tile<D, BLK, true>(cx, lds_k1, lds_v1, qf, oacc, mrow, lrow);
+      else
+        pair_tile<D, BLK, true>(cx, lds_k0, lds_v0, qf, oacc, mrow, lrow);
+    }
   }
 
   if (!active) return;
