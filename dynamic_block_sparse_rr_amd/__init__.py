@@ -71,6 +71,8 @@ def load():
         lib.rr_block_sparse_attn.restype = ctypes.c_int
         lib.rr_prefill.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.rr_prefill.restype = ctypes.c_int
+        lib.rr_mass_recall.argtypes = [PP, P, P, P, P, P, P]
+        lib.rr_mass_recall.restype = ctypes.c_int
         lib.rr_status_string.argtypes = [ctypes.c_int]
         lib.rr_status_string.restype = ctypes.c_char_p
         lib.rr_version.argtypes = []
@@ -142,6 +144,11 @@ def rr_prefill(p, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=No
     _check("rr_prefill", load().rr_prefill(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
         _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_mass_recall(p, q, k, row_count, col_idx, recall, stream=None):
+    _check("rr_mass_recall", load().rr_mass_recall(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx), _ptr(recall), _stream(stream)))
 
 
 def rr_status_string(status: int) -> str:

@@ -153,6 +153,17 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
   return run_attention(g, q, k, v, row_count, col_idx, out, ws, st);
 }
 
+rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, const int32_t* row_count,
+                         const int32_t* col_idx, float* recall, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !row_count || !col_idx || !recall) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(row_count) || !aligned16(col_idx) || !aligned16(recall))
+    return RR_ERR_INVALID_ARG;
+  return hip_status(rr::launch_recall(g, q, k, row_count, col_idx, recall, static_cast<hipStream_t>(stream)));
+}
+
 const char* rr_status_string(rr_status s) {
   switch (s) {
     case RR_OK: return "ok";

@@ -1,5 +1,5 @@
 // Internal launch interface between the host runtime (rr_host.cpp) and the
-// gfx950 kernels (search.hip, attn.hip). Not part of the public ABI.
+// gfx950 kernels (search.hip, attn.hip, recall.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +29,10 @@ hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStr
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const void* vt, const int32_t* row_count, const int32_t* col_idx,
                             void* out, hipStream_t st);
+
+// Selection quality: full-attention softmax mass inside the selected blocks.
+hipError_t launch_recall(const Geometry& g, const void* q, const void* k, const int32_t* row_count,
+                         const int32_t* col_idx, float* recall, hipStream_t st);
 
 // Kernel-side limits checked by the host before any launch.
 constexpr int kMaxSelectBlocks = 8192;  // LDS sort capacity of the select kernel (nb): 12 B per key

@@ -117,6 +117,25 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
                      int32_t* row_count, int32_t* col_idx, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * Mass recall of a selection against full attention: how much of the exact
+ * full-attention softmax mass the selected blocks hold (Figure 4 and Figure 5
+ * captions: full-attention ground truth next to the selected blocks). For
+ * query x of head h, r(x) is the share of its softmax over every admissible
+ * key (key <= x when causal; scale 1/sqrt(d)) that falls on keys of the
+ * row's selected blocks; recall[h][i] is the mean of r(x) over the B queries
+ * of query block i.
+ *   q, k        device inputs [L][Hq][d] and [L][Hkv][d] in p->dtype.
+ *   row_count, col_idx  device block lists as for rr_block_sparse_attn
+ *               (ascending; entries that break the order are not counted).
+ *   recall      device output float [Hq][nb].
+ * Cost: the scores of every candidate block (a dense causal Q K^T), about half
+ * the FLOPs of dense attention. p->S and p->tau are not used but must be valid.
+ * Needs no workspace.
+ */
+rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, const int32_t* row_count,
+                         const int32_t* col_idx, float* recall, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rr_status_string(rr_status s);
 

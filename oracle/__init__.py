@@ -71,6 +71,9 @@ def _load():
         lib.rro_attention.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P,
                                       ctypes.c_longlong, P, ctypes.c_int]
         lib.rro_attention.restype = ctypes.c_int
+        lib.rro_recall.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, ctypes.c_longlong, P,
+                                   ctypes.c_int]
+        lib.rro_recall.restype = ctypes.c_int
         lib.rro_max_threads.argtypes = []
         lib.rro_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -195,6 +198,40 @@ def attention(q, k, v, row_count, col_idx, *, B: int, causal: bool = True, rows=
         raise ValueError("block lists are not ascending / in range / causal")
     if rc:
         raise ValueError("rro_attention failed (%d)" % rc)
+    return out
+
+
+def mass_recall(q, k, row_count, col_idx, *, B: int, causal: bool = True, rows=None,
+                nthreads: int = 0) -> np.ndarray:
+    """Full-attention softmax mass inside the selected blocks, float64.
+
+    For each row (h, i): the mean over the B queries of query block i of the
+    fraction of query x's full-attention softmax mass (over every admissible
+    key) that falls on keys of the row's selected blocks. rows=None gives
+    [Hq][nb]; otherwise rows is an int array of (h, i) pairs and the result is
+    [len(rows)].
+    """
+    q = _f32(q)
+    k = _f32(k)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    nb = L // B
+    p = _problem(L, Hq, Hkv, d, 1, B, 1.0, causal, 0)
+    rc_ = np.ascontiguousarray(row_count, np.int32)
+    ci = np.ascontiguousarray(col_idx, np.int32)
+    if rows is None:
+        out = np.empty((Hq, nb), np.float64)
+        rp, n = None, 0
+    else:
+        rp = np.ascontiguousarray(rows, np.int32).reshape(-1, 2)
+        n = rp.shape[0]
+        out = np.empty((n,), np.float64)
+    rc = _load().rro_recall(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(rc_), _ptr(ci), _ptr(rp), int(n),
+                            _ptr(out), int(nthreads))
+    if rc == 3:
+        raise ValueError("block lists are not ascending / in range / causal")
+    if rc:
+        raise ValueError("rro_recall failed (%d)" % rc)
     return out
 
 

@@ -335,3 +335,82 @@ int rro_attention(const rro_problem* p, const float* Q, const float* K, const fl
   }
   return status;
 }
+
+/*
+ * Mass recall of the selection against full attention: the quantity behind
+ * the Figure 4 and Figure 5 captions (full-attention ground truth next to
+ * the blocks RRAttention selects). For query x of head h with logits
+ * a_y = Q[x,h] . K[y,g] / sqrt(d) over every admissible key y (y <= x with the
+ * causal flag), the full-attention softmax mass that falls on keys of the
+ * row's selected blocks is
+ *   r(x) = sum_{y selected} exp(a_y - max) / sum_{y admissible} exp(a_y - max).
+ * out[n] is the mean of r(x) over the B queries x of query block i for the
+ * n-th requested row (h, i) (rows: n_rows pairs h, i; NULL = every row, in
+ * [Hq][nb] order). float64, two passes (maximum, then the two sums).
+ */
+int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32_t* row_count,
+               const int32_t* col_idx, const int32_t* rows, long long n_rows, double* out,
+               int nthreads) {
+  if (check_problem(p) || !Q || !K || !row_count || !col_idx || !out) return 1;
+  if (check_lists(p, row_count, col_idx)) return 3;
+  const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, B = p->B;
+  const int nb = L / B, G = Hq / Hkv;
+  const double sigma = 1.0 / sqrt((double)d);
+  const long long total_rows = rows ? n_rows : (long long)Hq * nb;
+  int status = 0;
+  set_threads(nthreads);
+
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)L);
+    char* sel = (char*)malloc((size_t)nb);
+    if (!a || !sel) {
+#pragma omp atomic write
+      status = 2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long long n = 0; n < total_rows; ++n) {
+        int h, i;
+        if (rows) {
+          h = rows[2 * n];
+          i = rows[2 * n + 1];
+        } else {
+          h = (int)(n / nb);
+          i = (int)(n % nb);
+        }
+        if (h < 0 || h >= Hq || i < 0 || i >= nb) {
+          out[n] = NAN;
+          continue;
+        }
+        const int g = h / G;
+        const size_t row = (size_t)h * nb + i;
+        for (int j = 0; j < nb; ++j) sel[j] = 0;
+        for (int c = 0; c < row_count[row]; ++c) sel[col_idx[row * nb + c]] = 1;
+        double mean = 0.0;
+        for (int x = i * B; x < (i + 1) * B; ++x) {
+          const float* qv = Q + ((size_t)x * Hq + h) * d;
+          const int ny = p->causal ? x + 1 : L;
+          double mx = -INFINITY;
+          for (int y = 0; y < ny; ++y) {
+            const float* kv = K + ((size_t)y * Hkv + g) * d;
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e) dot += (double)qv[e] * (double)kv[e];
+            a[y] = sigma * dot;
+            if (a[y] > mx) mx = a[y];
+          }
+          double all = 0.0, in = 0.0;
+          for (int y = 0; y < ny; ++y) {
+            const double w = exp(a[y] - mx);
+            all += w;
+            if (sel[y / B]) in += w;
+          }
+          mean += in / all;
+        }
+        out[n] = mean / B;
+      }
+    }
+    free(a);
+    free(sel);
+  }
+  return status;
+}

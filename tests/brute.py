@@ -95,3 +95,27 @@ def masked_attention(q, k, v, mask_blocks: np.ndarray, *, B, causal=True) -> np.
         w = np.exp(a - a.max(axis=1, keepdims=True))
         out[:, h, :] = (w @ v[:, g, :]) / w.sum(axis=1, keepdims=True)
     return out
+
+
+def mass_recall(q, k, mask_blocks: np.ndarray, *, B, causal=True) -> np.ndarray:
+    """[Hq][nb] mean over each query block of the dense float64 softmax mass on the selected blocks.
+
+    Materialises the full softmax matrix with torch (float64) and sums it under
+    the block mask expanded to elements.
+    """
+    q = torch.from_numpy(np.asarray(q, np.float64))
+    k = torch.from_numpy(np.asarray(k, np.float64))
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    nb = L // B
+    elem = torch.from_numpy(np.kron(mask_blocks.astype(np.int8), np.ones((B, B), np.int8)).astype(bool))
+    out = np.zeros((Hq, nb))
+    for h in range(Hq):
+        a = (q[:, h, :] @ k[:, h // G, :].T) / math.sqrt(d)
+        if causal:
+            a = a.masked_fill(~torch.ones(L, L, dtype=torch.bool).tril(), float("-inf"))
+        w = torch.softmax(a, dim=1)
+        per_query = (w * elem[h]).sum(dim=1)  # [L]
+        out[h] = per_query.reshape(nb, B).mean(dim=1).numpy()
+    return out

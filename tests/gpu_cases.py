@@ -51,6 +51,15 @@ class GpuRun:
         torch.cuda.synchronize()
         return out.float().cpu().numpy()
 
+    def recall(self, row_count, col_idx):
+        """rr_mass_recall on the given lists: float [Hq][nb] on the host."""
+        rc = torch.from_numpy(np.ascontiguousarray(row_count, np.int32)).cuda()
+        ci = torch.from_numpy(np.ascontiguousarray(col_idx, np.int32)).cuda()
+        out = torch.full((self.w.Hq, self.w.nb), float("nan"), device="cuda")
+        rr.rr_mass_recall(self.p, self.qd, self.kd, rc, ci, out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
     def prefill(self):
         out, rc, ci = self.pre(self.qd, self.kd, self.vd)
         torch.cuda.synchronize()

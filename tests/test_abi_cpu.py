@@ -24,7 +24,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
-                            "rr_prefill", "rr_status_string", "rr_version"])
+                            "rr_prefill", "rr_mass_recall", "rr_status_string", "rr_version"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -79,6 +79,8 @@ def test_invalid_problems_rejected_on_host(kw, status):
     assert rc == status
     rc = lib.rr_prefill(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, 1 << 40, 0)
     assert rc == status
+    rc = lib.rr_mass_recall(ctypes.byref(p), fake, fake, fake, fake, fake, 0)
+    assert rc == status
 
 
 def test_pointer_and_workspace_checks():
@@ -95,6 +97,10 @@ def test_pointer_and_workspace_checks():
     assert lib.rr_prefill(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
     assert lib.rr_pattern_search(ctypes.byref(p), ok, ok, ok, ok, None, ok + 8, need, 0) == rr.RR_ERR_WORKSPACE
     assert lib.rr_workspace_bytes(None) == 0
+    # the recall harness: null / misaligned arguments, null problem
+    assert lib.rr_mass_recall(ctypes.byref(p), ok, ok, ok, ok, None, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_mass_recall(ctypes.byref(p), ok, ok + 4, ok, ok, ok, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_mass_recall(None, ok, ok, ok, ok, ok, 0) == rr.RR_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():
