@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--recall", action="store_true",
+                    help="also run rr_mass_recall on the produced lists: the full-attention softmax mass the "
+                         "selection holds per (head, query block), its statistics and its kernel time")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
                          "scaling HBM byte counters")
@@ -217,6 +220,26 @@ def main():
                  "speedup_vs_dense": round(dense_ms / ms_per_step, 3)}
         del drc, dci
         log(f"dense attention {dense_ms:.3f} ms")
+
+    if args.recall:
+        rec = torch.empty((w.Hq, w.nb), dtype=torch.float32, device="cuda")
+        rr.rr_mass_recall(p, qd, kd, pre.row_count, pre.col_idx, rec, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            rr.rr_mass_recall(p, qd, kd, pre.row_count, pre.col_idx, rec, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rec_ms = e0.elapsed_time(e1) / 3
+        r = rec.cpu().numpy()
+        cand = w.nb * (w.nb + 1) // 2 if w.causal else w.nb * w.nb
+        f_qk = 2.0 * w.B * w.B * w.d * cand * w.Hq  # scores of every candidate block
+        extra["mass_recall"] = {
+            "mean": round(float(r.mean()), 5), "min": round(float(r.min()), 5),
+            "p10": round(float(np.percentile(r, 10)), 5), "p50": round(float(np.percentile(r, 50)), 5),
+            "rows_below_0.5": int((r < 0.5).sum()), "rows": int(r.size),
+            "kernel_ms": round(rec_ms, 3), "score_tflops": round(f_qk / (rec_ms * 1e-3) / 1e12, 1)}
+        log(f"mass recall: mean {r.mean():.4f} min {r.min():.4f} ({rec_ms:.3f} ms)")
 
     line = {
         "metric": METRIC,
