@@ -134,6 +134,9 @@ def main():
     ap.add_argument("--recall", action="store_true",
                     help="also run rr_mass_recall on the produced lists: the full-attention softmax mass the "
                          "selection holds per (head, query block), its statistics and its kernel time")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
+                         "reported as cold_* fields, events only")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
                          "scaling HBM byte counters")
@@ -189,6 +192,28 @@ def main():
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     ms_per_step = wall * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (search {search_ms:.3f} ms, attention {attn_ms:.3f} ms)")
+
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    cold = {}
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cs, ca = [], []
+        for _ in range(max(3, args.steps)):
+            flush.fill_(1)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
+            e[1].record(stream)
+            rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            cs.append(e[0].elapsed_time(e[1]))
+            ca.append(e[1].elapsed_time(e[2]))
+        del flush
+        cold = {"cold_search_ms_median": round(float(np.median(cs)), 3),
+                "cold_attn_ms_median": round(float(np.median(ca)), 3),
+                "cold_step_ms_median": round(float(np.median(np.add(cs, ca))), 3)}
+        log(f"cold steps (after a 1 GiB write): search {np.median(cs):.3f} ms, attention {np.median(ca):.3f} ms")
 
     rc = pre.row_count.cpu().numpy()
     ci = pre.col_idx.cpu().numpy()
@@ -256,6 +281,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "B": w.B,
                    "S": w.S, "tau": tau, "causal": w.causal, "seed": w.seed, "batch": 1},
+        "step_ms_median_events": round(float(np.median(step_ms)), 3),
+        **cold,
         "search_ms": round(search_ms, 3),
         "attn_ms": round(attn_ms, 3),
         "search_share": round(search_ms / (search_ms + attn_ms), 4),
