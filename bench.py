@@ -134,6 +134,9 @@ def main():
     ap.add_argument("--recall", action="store_true",
                     help="also run rr_mass_recall on the produced lists: the full-attention softmax mass the "
                          "selection holds per (head, query block), its statistics and its kernel time")
+    ap.add_argument("--shared-mask", action="store_true",
+                    help="variant: every head of a KV head attends over the union of the group's selections "
+                         "(rr_share_group_lists runs inside the step, after the search)")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
                          "reported as cold_* fields, events only")
@@ -168,9 +171,23 @@ def main():
     pre = rr.Prefill(p)
     stream = torch.cuda.current_stream()
 
-    def step():
+    # the lists the attention reads: the search's own, or their union per KV head
+    if args.shared_mask:
+        arc, aci = torch.empty_like(pre.row_count), torch.empty_like(pre.col_idx)
+    else:
+        arc, aci = pre.row_count, pre.col_idx
+
+    def search():
         rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
-        rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+        if args.shared_mask:
+            rr.rr_share_group_lists(p, pre.row_count, pre.col_idx, arc, aci, stream=stream)
+
+    def attend():
+        rr.rr_block_sparse_attn(p, qd, kd, vd, arc, aci, pre.out, pre.ws, stream=stream)
+
+    def step():
+        search()
+        attend()
 
     for _ in range(args.warmup):
         step()
@@ -182,9 +199,9 @@ def main():
     t_start = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
-        rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
+        search()
         ev[s][1].record(stream)
-        rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+        attend()
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -202,9 +219,9 @@ def main():
             flush.fill_(1)
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record(stream)
-            rr.rr_pattern_search(p, qd, kd, pre.row_count, pre.col_idx, None, pre.ws, stream=stream)
+            search()
             e[1].record(stream)
-            rr.rr_block_sparse_attn(p, qd, kd, vd, pre.row_count, pre.col_idx, pre.out, pre.ws, stream=stream)
+            attend()
             e[2].record(stream)
             torch.cuda.synchronize()
             cs.append(e[0].elapsed_time(e[1]))
@@ -215,8 +232,8 @@ def main():
                 "cold_step_ms_median": round(float(np.median(np.add(cs, ca))), 3)}
         log(f"cold steps (after a 1 GiB write): search {np.median(cs):.3f} ms, attention {np.median(ca):.3f} ms")
 
-    rc = pre.row_count.cpu().numpy()
-    ci = pre.col_idx.cpu().numpy()
+    rc = arc.cpu().numpy()
+    ci = aci.cpu().numpy()
     f_comp, nblocks, ndiag = computed_flops(rc, ci, w.B, w.d, w.causal)
     causal_blocks = w.Hq * w.nb * (w.nb + 1) // 2 if w.causal else w.Hq * w.nb * w.nb
     pct = 100.0 * nblocks / causal_blocks
@@ -248,11 +265,11 @@ def main():
 
     if args.recall:
         rec = torch.empty((w.Hq, w.nb), dtype=torch.float32, device="cuda")
-        rr.rr_mass_recall(p, qd, kd, pre.row_count, pre.col_idx, rec, stream=stream)
+        rr.rr_mass_recall(p, qd, kd, arc, aci, rec, stream=stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(3):
-            rr.rr_mass_recall(p, qd, kd, pre.row_count, pre.col_idx, rec, stream=stream)
+            rr.rr_mass_recall(p, qd, kd, arc, aci, rec, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         rec_ms = e0.elapsed_time(e1) / 3
@@ -280,7 +297,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "B": w.B,
-                   "S": w.S, "tau": tau, "causal": w.causal, "seed": w.seed, "batch": 1},
+                   "S": w.S, "tau": tau, "causal": w.causal, "seed": w.seed, "batch": 1,
+                   **({"mask": "shared per KV head (union of the group's selections)"} if args.shared_mask else {})},
         "step_ms_median_events": round(float(np.median(step_ms)), 3),
         **cold,
         "search_ms": round(search_ms, 3),

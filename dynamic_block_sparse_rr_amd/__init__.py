@@ -73,6 +73,8 @@ def load():
         lib.rr_prefill.restype = ctypes.c_int
         lib.rr_mass_recall.argtypes = [PP, P, P, P, P, P, P]
         lib.rr_mass_recall.restype = ctypes.c_int
+        lib.rr_share_group_lists.argtypes = [PP, P, P, P, P, P]
+        lib.rr_share_group_lists.restype = ctypes.c_int
         lib.rr_status_string.argtypes = [ctypes.c_int]
         lib.rr_status_string.restype = ctypes.c_char_p
         lib.rr_version.argtypes = []
@@ -149,6 +151,12 @@ def rr_prefill(p, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=No
 def rr_mass_recall(p, q, k, row_count, col_idx, recall, stream=None):
     _check("rr_mass_recall", load().rr_mass_recall(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx), _ptr(recall), _stream(stream)))
+
+
+def rr_share_group_lists(p, row_count, col_idx, shared_row_count, shared_col_idx, stream=None):
+    _check("rr_share_group_lists", load().rr_share_group_lists(
+        ctypes.byref(p), _ptr(row_count), _ptr(col_idx), _ptr(shared_row_count), _ptr(shared_col_idx),
+        _stream(stream)))
 
 
 def rr_status_string(status: int) -> str:

@@ -164,6 +164,27 @@ rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, cons
   return hip_status(rr::launch_recall(g, q, k, row_count, col_idx, recall, static_cast<hipStream_t>(stream)));
 }
 
+rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, const int32_t* col_idx,
+                               int32_t* shared_row_count, int32_t* shared_col_idx, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!row_count || !col_idx || !shared_row_count || !shared_col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(row_count) || !aligned16(col_idx) || !aligned16(shared_row_count) || !aligned16(shared_col_idx))
+    return RR_ERR_INVALID_ARG;
+  // the outputs are written while other rows of the inputs are still read
+  const uintptr_t in0 = reinterpret_cast<uintptr_t>(col_idx), out0 = reinterpret_cast<uintptr_t>(shared_col_idx);
+  const uintptr_t ci_bytes = (uintptr_t)g.Hq * g.nb * g.nb * sizeof(int32_t);
+  const uintptr_t rc_bytes = (uintptr_t)g.Hq * g.nb * sizeof(int32_t);
+  const uintptr_t r0 = reinterpret_cast<uintptr_t>(row_count), s0 = reinterpret_cast<uintptr_t>(shared_row_count);
+  auto overlap = [](uintptr_t a, uintptr_t na, uintptr_t b, uintptr_t nb_) { return a < b + nb_ && b < a + na; };
+  if (overlap(in0, ci_bytes, out0, ci_bytes) || overlap(r0, rc_bytes, s0, rc_bytes) ||
+      overlap(in0, ci_bytes, s0, rc_bytes) || overlap(r0, rc_bytes, out0, ci_bytes))
+    return RR_ERR_INVALID_ARG;
+  return hip_status(rr::launch_union_lists(g, row_count, col_idx, shared_row_count, shared_col_idx,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 const char* rr_status_string(rr_status s) {
   switch (s) {
     case RR_OK: return "ok";

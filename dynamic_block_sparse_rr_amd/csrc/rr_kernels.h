@@ -24,6 +24,10 @@ hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, flo
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
                          int32_t* col_idx, hipStream_t st);
 
+// Variant: every head of a KV head gets the union of the group's selections.
+hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,
+                              int32_t* out_count, int32_t* out_idx, hipStream_t st);
+
 // Stage 2 launches.
 hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStream_t st);
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,

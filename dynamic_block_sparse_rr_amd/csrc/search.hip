@@ -401,6 +401,69 @@ __global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, i
   if (tid == 0) row_count[row] = ipart[255];
 }
 
+// Shared mask per KV head (a variant of the per-head masks, not on the pages:
+// the union of the G query heads' selected blocks of one query-block row,
+// given to every head of the group, so the heads of a KV head compute the
+// same blocks). One workgroup per (KV head g, query block i): the union is a
+// bitmap of nb bits in LDS (order-free bit sets), compacted in ascending order
+// with a prefix sum of the words' popcounts, and written to every head's row.
+__global__ void __launch_bounds__(256) union_lists_kernel(const int32_t* __restrict__ row_count,
+                                                          const int32_t* __restrict__ col_idx,
+                                                          int32_t* __restrict__ out_count,
+                                                          int32_t* __restrict__ out_idx, int nb, int G) {
+  extern __shared__ uint32_t smem_u[];
+  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t carry;
+  const int nw = (nb + 31) / 32;  // bitmap words
+  uint32_t* bits = smem_u;        // [nw]
+  uint32_t* base = smem_u + nw;   // [nw] exclusive prefix of the popcounts
+  const int g = blockIdx.x / nb, i = blockIdx.x % nb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int w = threadIdx.x; w < nw; w += 256) bits[w] = 0u;
+  if (threadIdx.x == 0) carry = 0u;
+  __syncthreads();
+  for (int hh = 0; hh < G; ++hh) {
+    const size_t row = (size_t)(g * G + hh) * nb + i;
+    const int cnt = min(max(row_count[row], 0), nb);
+    for (int c = threadIdx.x; c < cnt; c += 256) {
+      const int j = col_idx[row * nb + c];
+      if (j >= 0 && j < nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+  }
+  __syncthreads();
+  // exclusive prefix sum of the popcounts, 256 words per pass plus a carry
+  for (int w0 = 0; w0 < nw; w0 += 256) {
+    const int w = w0 + threadIdx.x;
+    const uint32_t c = w < nw ? (uint32_t)__popc(bits[w]) : 0u;
+    uint32_t v = c;  // inclusive scan: in-wave shuffles, then the wave totals in order
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int k = 0; k < wave; ++k) before += wsum[k];
+    if (w < nw) base[w] = before + v - c;
+    __syncthreads();
+    if (threadIdx.x == 255) carry = before + v;
+    __syncthreads();
+  }
+  const uint32_t total = carry;
+  for (int w = threadIdx.x; w < nw; w += 256) {
+    uint32_t m = bits[w];
+    uint32_t pos = base[w];
+    while (m) {
+      const int j = w * 32 + (__ffs(m) - 1);
+      m &= m - 1;
+      for (int hh = 0; hh < G; ++hh) out_idx[((size_t)(g * G + hh) * nb + i) * nb + pos] = j;
+      ++pos;
+    }
+  }
+  if (threadIdx.x < G) out_count[(size_t)(g * G + threadIdx.x) * nb + i] = (int32_t)total;
+}
+
 template <typename T, int D>
 hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, float* mass,
                            hipStream_t st) {
@@ -465,6 +528,14 @@ hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, in
   select_kernel<<<dim3((unsigned)(g.Hq * g.nb)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill,
                                                                  row_count, col_idx, g.nb, g.causal,
                                                                  g.tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,
+                              int32_t* out_count, int32_t* out_idx, hipStream_t st) {
+  const size_t lds = 2 * (size_t)((g.nb + 31) / 32) * sizeof(uint32_t);
+  union_lists_kernel<<<dim3((unsigned)(g.Hkv * g.nb)), 256, lds, st>>>(row_count, col_idx, out_count, out_idx,
+                                                                      g.nb, g.G);
   return hipGetLastError();
 }
 

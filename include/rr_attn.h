@@ -136,6 +136,21 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
 rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, const int32_t* row_count,
                          const int32_t* col_idx, float* recall, void* stream);
 
+/*
+ * Shared mask per KV head: a variant of the per-query-head masks above (the
+ * pages select per head; this is not on them). For every KV head g and query
+ * block i, the union of the blocks selected by the G = Hq / Hkv query heads
+ * of g in row i, written in ascending order to row (h, i) of every head h of
+ * g, so all heads of a KV head compute the same blocks.
+ *   row_count, col_idx                device input lists (format above).
+ *   shared_row_count, shared_col_idx  device output lists, same format; they
+ *                                     must not overlap the inputs.
+ * The outputs can be passed to rr_block_sparse_attn and rr_mass_recall as
+ * they are. p->S and p->tau are not used but must be valid. No workspace.
+ */
+rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, const int32_t* col_idx,
+                               int32_t* shared_row_count, int32_t* shared_col_idx, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rr_status_string(rr_status s);
 

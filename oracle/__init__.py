@@ -235,6 +235,30 @@ def mass_recall(q, k, row_count, col_idx, *, B: int, causal: bool = True, rows=N
     return out
 
 
+def share_group_lists(row_count, col_idx, G: int):
+    """Shared mask per KV head (a variant; the pages' masks are per query head).
+
+    Row (h, i) of every head h of KV head g = h // G gets the ascending union of
+    the blocks the G heads of g selected in row i. Returns (row_count,
+    col_idx) in the same format, unused entries -1.
+    """
+    rc = np.asarray(row_count, np.int32)
+    ci = np.asarray(col_idx, np.int32)
+    Hq, nb = rc.shape
+    out_rc = np.zeros_like(rc)
+    out_ci = np.full_like(ci, -1)
+    for g in range(Hq // G):
+        for i in range(nb):
+            u = set()
+            for h in range(g * G, (g + 1) * G):
+                u.update(int(j) for j in ci[h, i, : rc[h, i]])
+            js = sorted(u)
+            for h in range(g * G, (g + 1) * G):
+                out_rc[h, i] = len(js)
+                out_ci[h, i, : len(js)] = js
+    return out_rc, out_ci
+
+
 def full_lists(L: int, Hq: int, B: int, causal: bool = True):
     """Lists that select every candidate block (the dense pattern)."""
     nb = L // B

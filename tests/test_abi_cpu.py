@@ -24,7 +24,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
-                            "rr_prefill", "rr_mass_recall", "rr_status_string", "rr_version"])
+                            "rr_prefill", "rr_mass_recall", "rr_share_group_lists", "rr_status_string",
+                            "rr_version"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -81,6 +82,8 @@ def test_invalid_problems_rejected_on_host(kw, status):
     assert rc == status
     rc = lib.rr_mass_recall(ctypes.byref(p), fake, fake, fake, fake, fake, 0)
     assert rc == status
+    rc = lib.rr_share_group_lists(ctypes.byref(p), fake, fake, fake << 4, fake << 5, 0)
+    assert rc == status
 
 
 def test_pointer_and_workspace_checks():
@@ -101,6 +104,12 @@ def test_pointer_and_workspace_checks():
     assert lib.rr_mass_recall(ctypes.byref(p), ok, ok, ok, ok, None, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_mass_recall(ctypes.byref(p), ok, ok + 4, ok, ok, ok, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_mass_recall(None, ok, ok, ok, ok, ok, 0) == rr.RR_ERR_INVALID_ARG
+    # shared lists: null, misaligned, and outputs overlapping the inputs
+    far = 1 << 40
+    assert lib.rr_share_group_lists(ctypes.byref(p), ok, ok, None, far, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_share_group_lists(ctypes.byref(p), ok, ok + 4, far, far << 1, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_share_group_lists(ctypes.byref(p), ok, far, ok + 1024, far << 1, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_share_group_lists(ctypes.byref(p), ok, far, far << 1, far + 4096, 0) == rr.RR_ERR_INVALID_ARG
 
 
 def test_binding_refuses_cpu_tensors():
