@@ -65,7 +65,7 @@ def _load():
         lib.rro_round_bf16.restype = ctypes.c_float
         lib.rro_pool.argtypes = [ctypes.POINTER(_Problem), P, P]
         lib.rro_pool.restype = ctypes.c_int
-        lib.rro_search.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, P, P, P, P,
+        lib.rro_search.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, P, P, P, P, P,
                                    ctypes.c_int]
         lib.rro_search.restype = ctypes.c_int
         lib.rro_attention.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P,
@@ -107,7 +107,7 @@ def pool(k, S: int, round_bf16: bool) -> np.ndarray:
     """Stride-mean pooled keys [L/S][Hkv][d] (float32 values)."""
     k = _f32(k)
     L, Hkv, d = k.shape
-    out = np.empty((L // S, Hkv, d), np.float32)
+    out = np.empty((-(-L // S), Hkv, d), np.float32)
     p = _problem(L, Hkv, Hkv, d, S, S, 1.0, 1, round_bf16)
     rc = _load().rro_pool(ctypes.byref(p), _ptr(k), _ptr(out))
     if rc:
@@ -138,17 +138,20 @@ class SearchResult:
 
 
 def search(q, k, *, S: int, B: int, tau: float, causal: bool = True, round_bf16: bool,
-           nthreads: int = 0, extras: bool = True, row_mask=None) -> SearchResult:
+           nthreads: int = 0, extras: bool = True, row_mask=None, tau_per_head=None) -> SearchResult:
     """Round-robin pattern search with Top-tau selection (float32 arithmetic).
 
     row_mask: optional bool [Hq][nb]; only those rows are searched (the others
     get row_count 0), for spot checks of large layers.
+    tau_per_head: optional [Hq] thresholds used in place of tau.
+    L need not be a multiple of B or S: nb = ceil(L / B), and the last block
+    and stride may be short.
     """
     q = _f32(q)
     k = _f32(k)
     L, Hq, d = q.shape
     Hkv = k.shape[1]
-    nb = L // B
+    nb = -(-L // B)
     p = _problem(L, Hq, Hkv, d, S, B, tau, causal, round_bf16)
     row_count = np.zeros((Hq, nb), np.int32)
     col_idx = np.zeros((Hq, nb, nb), np.int32)
@@ -158,13 +161,14 @@ def search(q, k, *, S: int, B: int, tau: float, causal: bool = True, round_bf16:
         cplus = np.zeros((Hq, nb, nb), np.float32)
         rank = np.zeros((Hq, nb, nb), np.int32)
         total = np.zeros((Hq, nb), np.float32)
-        kbar = np.zeros((L // S, Hkv, d), np.float32)
+        kbar = np.zeros((-(-L // S), Hkv, d), np.float32)
     else:
         cminus = cplus = rank = total = kbar = None
     rm = None if row_mask is None else np.ascontiguousarray(row_mask, dtype=np.uint8).reshape(Hq, nb)
+    th = None if tau_per_head is None else np.ascontiguousarray(tau_per_head, dtype=np.float32).reshape(Hq)
     rc = _load().rro_search(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx),
                             _ptr(mass), _ptr(cminus), _ptr(cplus), _ptr(rank), _ptr(total),
-                            _ptr(kbar), _ptr(rm), int(nthreads))
+                            _ptr(kbar), _ptr(rm), _ptr(th), int(nthreads))
     if rc:
         raise ValueError("rro_search failed (%d)" % rc)
     return SearchResult(row_count, col_idx, mass, cminus, cplus, rank, total, kbar)
@@ -215,7 +219,7 @@ def mass_recall(q, k, row_count, col_idx, *, B: int, causal: bool = True, rows=N
     k = _f32(k)
     L, Hq, d = q.shape
     Hkv = k.shape[1]
-    nb = L // B
+    nb = -(-L // B)
     p = _problem(L, Hq, Hkv, d, 1, B, 1.0, causal, 0)
     rc_ = np.ascontiguousarray(row_count, np.int32)
     ci = np.ascontiguousarray(col_idx, np.int32)
@@ -261,7 +265,7 @@ def share_group_lists(row_count, col_idx, G: int):
 
 def full_lists(L: int, Hq: int, B: int, causal: bool = True):
     """Lists that select every candidate block (the dense pattern)."""
-    nb = L // B
+    nb = -(-L // B)
     row_count = np.zeros((Hq, nb), np.int32)
     col_idx = np.full((Hq, nb, nb), -1, np.int32)
     for i in range(nb):

@@ -39,6 +39,13 @@
  * Layout: Q [L][Hq][d], K and V [L][Hkv][d], batch 1; query head h reads KV
  * head h / (Hq / Hkv). Block lists: row_count [Hq][nb], col_idx [Hq][nb][nb]
  * holding the selected key blocks of row (h, i) in ascending order.
+ *
+ * Ragged lengths (not on the pages; the plainest extension): L need not be a
+ * multiple of B or S. nb = ceil(L / B) and ns = ceil(L / S); the last stride
+ * pools the tokens it has (their mean), the last key block holds the strides
+ * and keys that exist, keys at or past L are never attended, and the last
+ * query block (kept whole) has L - (nb - 1) B queries. A threshold per query
+ * head may replace tau.
  */
 #include <math.h>
 #include <stdint.h>
@@ -76,7 +83,7 @@ static int check_problem(const rro_problem* p) {
   if (!p) return 1;
   if (p->L <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0 || p->S <= 0 || p->B <= 0) return 1;
   if (p->Hq % p->Hkv) return 1;
-  if (p->B % p->S || p->L % p->B) return 1;
+  if (p->B % p->S) return 1; /* L need not be a multiple of B or S: the last block and stride may be short */
   if (!(p->tau > 0.0f)) return 1;
   return 0;
 }
@@ -97,18 +104,25 @@ int rro_max_threads(void) {
 #endif
 }
 
-/* Stride pooling: Kbar[t][k][e] = mean over u < S of K[t*S+u][k][e]. */
+/* strides and blocks of a sequence of L tokens; the last of each may be short */
+static int n_strides(const rro_problem* p) { return (p->L + p->S - 1) / p->S; }
+static int n_blocks(const rro_problem* p) { return (p->L + p->B - 1) / p->B; }
+
+/* Stride pooling: Kbar[t][k][e] = mean over the tokens u of stride t
+ * (u < S, and t*S + u < L for a short last stride) of K[t*S+u][k][e]. */
 int rro_pool(const rro_problem* p, const float* K, float* Kbar) {
   if (check_problem(p) || !K || !Kbar) return 1;
-  const int S = p->S, H = p->Hkv, d = p->d, ns = p->L / p->S;
-  for (int t = 0; t < ns; ++t)
+  const int S = p->S, H = p->Hkv, d = p->d, ns = n_strides(p);
+  for (int t = 0; t < ns; ++t) {
+    const int cnt = p->L - t * S < S ? p->L - t * S : S;
     for (int k = 0; k < H; ++k)
       for (int e = 0; e < d; ++e) {
         float acc = 0.0f;
-        for (int u = 0; u < S; ++u) acc += K[((size_t)(t * S + u) * H + k) * d + e];
-        float mean = acc / (float)S;
+        for (int u = 0; u < cnt; ++u) acc += K[((size_t)(t * S + u) * H + k) * d + e];
+        float mean = acc / (float)cnt;
         Kbar[((size_t)t * H + k) * d + e] = p->round_bf16 ? rro_round_bf16(mean) : mean;
       }
+  }
   return 0;
 }
 
@@ -136,14 +150,20 @@ static int by_mass_desc(const void* a, const void* b) {
  *   total [Hq][nb]              the row total used for the cut,
  *   kbar [L/S][Hkv][d]          the pooled keys,
  *   row_mask [Hq][nb]           compute only rows with a nonzero entry (others
- *                               get row_count 0 and are otherwise untouched).
+ *                               get row_count 0 and are otherwise untouched),
+ *   tau_heads [Hq]              a threshold per query head in place of p->tau.
+ * With L not a multiple of B the last key block holds fewer strides; the
+ * searched rows (every query block but the last) are full blocks, so their
+ * sampled queries always exist.
  */
 int rro_search(const rro_problem* p, const float* Q, const float* K, int32_t* row_count,
                int32_t* col_idx, float* mass, float* cminus, float* cplus, int32_t* rank,
-               float* total, float* kbar_out, const uint8_t* row_mask, int nthreads) {
+               float* total, float* kbar_out, const uint8_t* row_mask, const float* tau_heads,
+               int nthreads) {
   if (check_problem(p) || !Q || !K || !row_count || !col_idx || !mass) return 1;
   const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, S = p->S, B = p->B;
-  const int ns = L / S, nb = L / B, r = B / S, G = Hq / Hkv;
+  const int ns = n_strides(p), nb = n_blocks(p), r = B / S, G = Hq / Hkv;
+  (void)L;
   const float sigma = 1.0f / sqrtf((float)d);
   float* Kbar = (float*)malloc(sizeof(float) * (size_t)ns * Hkv * d);
   if (!Kbar) return 2;
@@ -213,11 +233,12 @@ int rro_search(const rro_problem* p, const float* Q, const float* K, int32_t* ro
         }
         const float T = run;
         if (total) total[row] = T;
-        const float thr = p->tau * T;
+        const float tau = tau_heads ? tau_heads[h] : p->tau;
+        const float thr = tau * T;
         for (int j = 0; j < nb; ++j) keep[j] = 0;
         if (rank)
           for (int j = ncand; j < nb; ++j) rank[row * nb + j] = -1;
-        if (i == nb - 1 || p->tau >= 1.0f) {
+        if (i == nb - 1 || tau >= 1.0f) {
           for (int j = 0; j < ncand; ++j) keep[j] = 1;
         } else {
           float before = 0.0f;
@@ -245,7 +266,7 @@ int rro_search(const rro_problem* p, const float* Q, const float* K, int32_t* ro
 
 /* Lists must be ascending, in range and (causal) at most the query block. */
 static int check_lists(const rro_problem* p, const int32_t* row_count, const int32_t* col_idx) {
-  const int nb = p->L / p->B;
+  const int nb = n_blocks(p);
   for (long long row = 0; row < (long long)p->Hq * nb; ++row) {
     const int i = (int)(row % nb);
     const int cnt = row_count[row];
@@ -270,7 +291,7 @@ int rro_attention(const rro_problem* p, const float* Q, const float* K, const fl
   if (check_problem(p) || !Q || !K || !V || !row_count || !col_idx || !out) return 1;
   if (check_lists(p, row_count, col_idx)) return 3;
   const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, B = p->B;
-  const int nb = L / B, G = Hq / Hkv;
+  const int nb = n_blocks(p), G = Hq / Hkv;
   const double sigma = 1.0 / sqrt((double)d);
   const long long total_rows = rows ? n_rows : (long long)L * Hq;
   int status = 0;
@@ -307,7 +328,7 @@ int rro_attention(const rro_problem* p, const float* Q, const float* K, const fl
         double mx = -INFINITY;
         for (int c = 0; c < row_count[row]; ++c) {
           const int j = col_idx[row * nb + c];
-          for (int y = j * B; y < (j + 1) * B; ++y) {
+          for (int y = j * B; y < (j + 1) * B && y < L; ++y) {
             if (p->causal && y > x) break;
             const float* kv = K + ((size_t)y * Hkv + g) * d;
             double dot = 0.0;
@@ -346,7 +367,8 @@ int rro_attention(const rro_problem* p, const float* Q, const float* K, const fl
  *   r(x) = sum_{y selected} exp(a_y - max) / sum_{y admissible} exp(a_y - max).
  * out[n] is the mean of r(x) over the B queries x of query block i for the
  * n-th requested row (h, i) (rows: n_rows pairs h, i; NULL = every row, in
- * [Hq][nb] order). float64, two passes (maximum, then the two sums).
+ * [Hq][nb] order); a short last block averages over the queries it has.
+ * float64, two passes (maximum, then the two sums).
  */
 int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32_t* row_count,
                const int32_t* col_idx, const int32_t* rows, long long n_rows, double* out,
@@ -354,7 +376,7 @@ int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32
   if (check_problem(p) || !Q || !K || !row_count || !col_idx || !out) return 1;
   if (check_lists(p, row_count, col_idx)) return 3;
   const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, B = p->B;
-  const int nb = L / B, G = Hq / Hkv;
+  const int nb = n_blocks(p), G = Hq / Hkv;
   const double sigma = 1.0 / sqrt((double)d);
   const long long total_rows = rows ? n_rows : (long long)Hq * nb;
   int status = 0;
@@ -387,7 +409,8 @@ int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32
         for (int j = 0; j < nb; ++j) sel[j] = 0;
         for (int c = 0; c < row_count[row]; ++c) sel[col_idx[row * nb + c]] = 1;
         double mean = 0.0;
-        for (int x = i * B; x < (i + 1) * B; ++x) {
+        const int xend = (i + 1) * B < L ? (i + 1) * B : L;
+        for (int x = i * B; x < xend; ++x) {
           const float* qv = Q + ((size_t)x * Hq + h) * d;
           const int ny = p->causal ? x + 1 : L;
           double mx = -INFINITY;
@@ -406,7 +429,7 @@ int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32
           }
           mean += in / all;
         }
-        out[n] = mean / B;
+        out[n] = mean / (xend - i * B);
       }
     }
     free(a);

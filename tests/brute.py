@@ -119,3 +119,57 @@ def mass_recall(q, k, mask_blocks: np.ndarray, *, B, causal=True) -> np.ndarray:
         per_query = (w * elem[h]).sum(dim=1)  # [L]
         out[h] = per_query.reshape(nb, B).mean(dim=1).numpy()
     return out
+
+
+def block_mass_ragged(q, k, *, S, B, causal=True) -> np.ndarray:
+    """block_mass for any L (float inputs): the last stride and block may be short.
+
+    Pooled scores are the mean of the full logits over the tokens each stride
+    has (q . mean(k) = mean(q . k)); key block j covers the strides
+    t in [j*B/S, (j+1)*B/S) that exist. Rows i < nb-1 only (the last is 0).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    ns, nb, r = -(-L // S), -(-L // B), B // S
+    out = np.zeros((Hq, nb, nb))
+    stride_of = np.arange(L) // S
+    cnt = np.bincount(stride_of, minlength=ns).astype(np.float64)
+    for h in range(Hq):
+        g = h // G
+        pos = np.array([s * S + (h % S) for s in range((nb - 1) * r)], np.int64)
+        full = (q[pos, h, :] @ k[:, g, :].T) / math.sqrt(d)        # [(nb-1) r][L]
+        z = np.zeros((len(pos), ns))
+        np.add.at(z, (slice(None), stride_of), full)               # sum over each stride's tokens
+        z /= cnt[None, :]
+        if causal:
+            z = np.where(np.arange(ns)[None, :] <= np.arange(len(pos))[:, None], z, -np.inf)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        blk = np.zeros((len(pos), nb))
+        np.add.at(blk, (slice(None), np.arange(ns) // r), p)
+        out[h, : nb - 1] = blk.reshape(nb - 1, r, nb).mean(axis=1)
+    return out
+
+
+def masked_attention_ragged(q, k, v, mask_blocks: np.ndarray, *, B, causal=True) -> np.ndarray:
+    """masked_attention for any L: the block mask is expanded to nb*B elements and cut at L."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    L, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((L, Hq, d))
+    elem = np.kron(mask_blocks.astype(np.int8), np.ones((B, B), np.int8)).astype(bool)[:, :L, :L]
+    if causal:
+        elem &= np.tril(np.ones((L, L), bool))[None]
+    for h in range(Hq):
+        g = h // G
+        a = (q[:, h, :] @ k[:, g, :].T) / math.sqrt(d)
+        a = np.where(elem[h], a, -np.inf)
+        w = np.exp(a - a.max(axis=1, keepdims=True))
+        out[:, h, :] = (w @ v[:, g, :]) / w.sum(axis=1, keepdims=True)
+    return out
