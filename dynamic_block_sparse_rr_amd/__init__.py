@@ -38,7 +38,7 @@ class Problem(ctypes.Structure):
 
     @property
     def nb(self) -> int:
-        return self.L // self.B
+        return -(-self.L // self.B)  # the last block may be short
 
     def __repr__(self):
         return ("Problem(L=%d, Hq=%d, Hkv=%d, d=%d, S=%d, B=%d, tau=%g, causal=%d, dtype=%d)"
@@ -75,6 +75,12 @@ def load():
         lib.rr_mass_recall.restype = ctypes.c_int
         lib.rr_share_group_lists.argtypes = [PP, P, P, P, P, P]
         lib.rr_share_group_lists.restype = ctypes.c_int
+        lib.rr_pattern_search_heads.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_pattern_search_heads.restype = ctypes.c_int
+        lib.rr_workspace_bytes_varlen.argtypes = [PP, ctypes.c_int32, P]
+        lib.rr_workspace_bytes_varlen.restype = ctypes.c_size_t
+        lib.rr_prefill_varlen.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_prefill_varlen.restype = ctypes.c_int
         lib.rr_status_string.argtypes = [ctypes.c_int]
         lib.rr_status_string.restype = ctypes.c_char_p
         lib.rr_version.argtypes = []
@@ -157,6 +163,32 @@ def rr_share_group_lists(p, row_count, col_idx, shared_row_count, shared_col_idx
     _check("rr_share_group_lists", load().rr_share_group_lists(
         ctypes.byref(p), _ptr(row_count), _ptr(col_idx), _ptr(shared_row_count), _ptr(shared_col_idx),
         _stream(stream)))
+
+
+def rr_pattern_search_heads(p, q, k, tau_per_head, row_count, col_idx, block_mass, ws, ws_bytes=None,
+                            stream=None):
+    _check("rr_pattern_search_heads", load().rr_pattern_search_heads(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(tau_per_head), _ptr(row_count), _ptr(col_idx), _ptr(block_mass),
+        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def _lens(seq_lens):
+    import numpy as np
+
+    a = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def rr_workspace_bytes_varlen(p: Problem, seq_lens) -> int:
+    a, ptr = _lens(seq_lens)
+    return int(load().rr_workspace_bytes_varlen(ctypes.byref(p), int(a.size), ptr))
+
+
+def rr_prefill_varlen(p, seq_lens, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=None):
+    a, ptr = _lens(seq_lens)
+    _check("rr_prefill_varlen", load().rr_prefill_varlen(
+        ctypes.byref(p), int(a.size), ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
+        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
 
 
 def rr_status_string(status: int) -> str:

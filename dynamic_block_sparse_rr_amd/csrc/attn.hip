@@ -62,7 +62,7 @@ __host__ __device__ __forceinline__ int key_of_pos(int p) {
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
-                                                          __bf16* __restrict__ vt, int Hkv, int nb) {
+                                                          __bf16* __restrict__ vt, int Hkv, int nb, int L) {
   // one workgroup per (g, key block j); tile BLK keys x D channels
   __shared__ uint16_t tile[BLK][D + 2];
   const int j = blockIdx.x % nb;
@@ -71,7 +71,10 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
   constexpr int CH = D / 8;  // 16-byte chunks per key row
   for (int n = threadIdx.x; n < BLK * CH; n += 256) {
     const int key = n / CH, c = n % CH;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(src + ((size_t)(j * BLK + key) * Hkv + g) * D + c * 8);
+    // keys past the end of a short last block are zero (their probabilities are zero too)
+    const u32x4 w = j * BLK + key < L
+                        ? *reinterpret_cast<const u32x4*>(src + ((size_t)(j * BLK + key) * Hkv + g) * D + c * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       tile[key][c * 8 + 2 * e] = (uint16_t)(w[e] & 0xffffu);
@@ -139,27 +142,42 @@ struct AttnCtx {
 // per copy / chunks per row. Its swizzled chunk is chunk0 ^ ((n * RPC) mod
 // CH) because row0 < RPC, and chunk bits (16-byte units below the row size)
 // do not overlap row bits, hence the XOR on the offset.
+// Buffer descriptor over `bytes` bytes from p (raw addressing, no stride;
+// reads beyond the range return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, (int)bytes, 0x00020000);
+}
+
 template <int D, int BLK, int CH>
-__device__ __forceinline__ void copy_tile(const AttnCtx<D, BLK>& cx, const uint8_t* src, uint32_t off,
+__device__ __forceinline__ void copy_tile(const AttnCtx<D, BLK>& cx, __amdgpu_buffer_rsrc_t src, uint32_t off,
                                           uint32_t step, uint8_t* dst) {
   constexpr int RPC = AttnCtx<D, BLK>::NTHR / CH;
 #pragma unroll
   for (int n = 0; n < AttnCtx<D, BLK>::NDMA; ++n)
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const void*>((src + (size_t)(n * step)) + (off ^ (((n * RPC) & (CH - 1)) << 4))),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src,
         reinterpret_cast<__attribute__((address_space(3))) void*>(
             reinterpret_cast<uintptr_t>(dst + (n * AttnCtx<D, BLK>::NTHR + cx.wave * 64) * 16)),
-        16, 0, 0);
+        16, (int)(n * step + (off ^ (((n * RPC) & (CH - 1)) << 4))), 0, 0, 0);
+}
+
+// Bytes of a K tile from its first byte at offset tile_start of the K tensor
+// (k_bytes long): `full` when the tile lies inside it, else cut where it ends
+// (a short last block then reads zeros).
+__device__ __forceinline__ uint32_t k_tile_bytes(size_t tile_start, size_t k_bytes, uint32_t full) {
+  return tile_start + full <= k_bytes ? full : (uint32_t)(k_bytes - tile_start);
 }
 
 // One key block. On entry K (and possibly V) copies of this block are in
-// flight; next_k / next_v are the sources of the following block (null at the
-// end). diag: the key block is the query block itself under the causal flag,
-// keys after the query are masked.
+// flight; next_k / next_v are the descriptors of the following block's tiles
+// (has_next false at the end). masked: keys with index > klim inside the
+// block are masked (the causal diagonal block: klim = the lane's query row;
+// a short last block: klim = its last key).
 template <int D, int BLK>
 __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x8 (&qf)[D / 16],
-                                          f32x16 (&oacc)[D / 32], float& mrow, float& lrow,
-                                          const uint8_t* next_k, const uint8_t* next_v, bool diag) {
+                                          f32x16 (&oacc)[D / 32], float& mrow, float& lrow, bool has_next,
+                                          __amdgpu_buffer_rsrc_t next_k, __amdgpu_buffer_rsrc_t next_v, bool masked,
+                                          int klim) {
   constexpr int MT = AttnCtx<D, BLK>::MT;
   constexpr int NT = AttnCtx<D, BLK>::NT;
   constexpr int DK = AttnCtx<D, BLK>::DK;
@@ -187,16 +205,16 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   }
   // every wave is done with the K buffer: the next block's K may land in it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (next_k) copy_tile<D, BLK, AttnCtx<D, BLK>::KCH>(cx, next_k, cx.koff, cx.kstep, cx.lds_k);
+  if (has_next) copy_tile<D, BLK, AttnCtx<D, BLK>::KCH>(cx, next_k, cx.koff, cx.kstep, cx.lds_k);
 
   // online softmax in base 2 (scale folded into cscale)
-  if (diag) {
+  if (masked) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
-        if (key > cx.qr) sacc[mt][v] = -INFINITY;
+        if (key > klim) sacc[mt][v] = -INFINITY;
       }
   }
   float tmax = -INFINITY;
@@ -236,7 +254,7 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
   // V of this block has landed (the next block's K may still be in flight)
-  if (next_k)
+  if (has_next)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NDMA) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -257,14 +275,14 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   }
   // every wave is done with the V buffer: the next block's V may land in it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (next_v) copy_tile<D, BLK, AttnCtx<D, BLK>::VCH>(cx, next_v, cx.voff, cx.vstep, cx.lds_v);
+  if (has_next) copy_tile<D, BLK, AttnCtx<D, BLK>::VCH>(cx, next_v, cx.voff, cx.vstep, cx.lds_v);
 }
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale) {
+    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
   typedef AttnCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   constexpr int VCH = C::VCH;
@@ -308,10 +326,13 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
 
   bf16x8 qf[C::DK];
-  {
+  if (x < L) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
+  } else {  // past the end of a short last block: computed, never stored
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
   }
 
   const size_t row = (size_t)h * nb + i;
@@ -321,6 +342,13 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
   const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
+  const size_t k_bytes = (size_t)L * Hkv * D * 2;    // the whole K tensor
+  const uint32_t kfull = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+  auto krsrc = [&](int jj) {
+    return tile_rsrc(kg + (size_t)jj * kstride, k_tile_bytes((size_t)g * D * 2 + (size_t)jj * kstride, k_bytes, kfull));
+  };
+  auto vrsrc = [&](int jj) { return tile_rsrc(vg + (size_t)jj * C::TILE, C::TILE); };
+  const int ltail = L - (nb - 1) * BLK;  // keys in the last block (BLK unless it is short)
 
   f32x16 oacc[C::NT];
 #pragma unroll
@@ -330,20 +358,27 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // queries are in registers
   int j = cnt > 0 ? min(max(lst[0], 0), jmax) : 0;
   if (cnt > 0) {
-    copy_tile<D, BLK, KCH>(cx, kg + j * kstride, cx.koff, cx.kstep, lds_k);
-    copy_tile<D, BLK, VCH>(cx, vg + (size_t)j * C::TILE, cx.voff, cx.vstep, lds_v);
+    copy_tile<D, BLK, KCH>(cx, krsrc(j), cx.koff, cx.kstep, lds_k);
+    copy_tile<D, BLK, VCH>(cx, vrsrc(j), cx.voff, cx.vstep, lds_v);
   }
-  // Lists are ascending, so under the causal flag only the last entry can be
-  // the diagonal block: the loop never masks, the peeled last entry may.
+  // Lists are ascending, so only the last entry can need a mask (the causal
+  // diagonal block, or a short last block): the loop never masks, the peeled
+  // last entry may.
   for (int c = 0; c + 1 < cnt; ++c) {
     const int jn = min(max(lst[c + 1], 0), jmax);
-    attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, kg + jn * kstride, vg + (size_t)jn * C::TILE, false);
+    attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, true, krsrc(jn), vrsrc(jn), false, BLK - 1);
     j = jn;
   }
-  if (cnt > 0) attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, nullptr, nullptr, causal && j == i);
+  if (cnt > 0) {
+    const bool diag = causal && j == i;
+    const bool shortblk = j == nb - 1 && ltail < BLK;
+    attn_tile<D, BLK>(cx, qf, oacc, mrow, lrow, false, krsrc(j), vrsrc(j), diag || shortblk,
+                      diag ? cx.qr : ltail - 1);
+  }
 
   const float ltot = lrow + __shfl_xor(lrow, 32);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  if (x >= L) return;
   uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
 #pragma unroll
   for (int t = 0; t < C::NT; ++t) {
@@ -411,17 +446,13 @@ __device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, __amdgpu_bu
         16, (int)(n * step + (off ^ (((n * RPC) & (CH - 1)) << 4))), 0, 0, 0);
 }
 
-// Buffer descriptor over `bytes` bytes from p (raw addressing, no stride;
-// reads beyond the range return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), 0, (int)bytes, 0x00020000);
-}
-
 // One key block for one wave, operands already in LDS (no barriers inside).
-template <int D, int BLK, bool DIAG>
+// MASK: keys with index > klim inside the block are masked (the causal
+// diagonal block: the lane's query row; a short last block: its last key).
+template <int D, int BLK, bool MASK>
 __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8_t* lds_k, const uint8_t* lds_v,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& mrow,
-                                          float& lrow) {
+                                          float& lrow, int klim) {
   typedef PairCtx<D, BLK> C;
   constexpr int MT = C::MT;
   constexpr int NT = C::NT;
@@ -452,13 +483,13 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
-  if (DIAG) {
+  if (MASK) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
-        if (key > cx.qr) sacc[mt][v] = -INFINITY;
+        if (key > klim) sacc[mt][v] = -INFINITY;
       }
   }
   float tmax = -INFINITY;
@@ -544,7 +575,7 @@ template <int D, int BLK>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale) {
+    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
   typedef PairCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   constexpr int VCH = C::VCH;
@@ -586,7 +617,7 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
 
   bf16x8 qf[C::DK];
-  if (active) {
+  if (active && x < L) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
@@ -596,8 +627,12 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   }
 
   // the two block lists, merged on the fly (all values wave-uniform)
+  const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
   const int jlast = causal ? i : nb - 1;  // largest admissible key block
-  const int jdiag = causal ? i : nb;      // the masked block, if any
+  // the masked block, if any: the causal diagonal, else a short last block;
+  // either way the last entry of both ascending lists
+  const int jdiag = causal ? i : (ltail < BLK ? nb - 1 : nb);
+  const int klim = causal ? cx.qr : ltail - 1;
   const size_t rowA = (size_t)hA * nb + i, rowB = (size_t)hB * nb + i;
   const int cntA = min(max(row_count[rowA], 0), nb);
   const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
@@ -624,8 +659,10 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   // K rows of block j start at kg + j*kstride (row pitch Hkv*d*2 bytes); its Vt
   // tile is the contiguous TILE bytes at vg + j*TILE
   const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+  const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
   auto copy_block = [&](int jb_, uint8_t* kdst, uint8_t* vdst) {
-    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jb_ * kstride, kbytes), cx.koff, cx.kstep, kdst);
+    const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jb_ * kstride, k_bytes, kbytes);
+    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jb_ * kstride, kb), cx.koff, cx.kstep, kdst);
     pair_copy<D, BLK, VCH>(cx, tile_rsrc(vg + (size_t)jb_ * C::TILE, C::TILE), cx.voff, cx.vstep, vdst);
   };
   int j = min(ja, jb);
@@ -648,7 +685,7 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
     if (jn <= jlast) copy_block(jn, kn, vn);
-    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, kc, vc, qf, oacc, mrow, lrow);
+    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, kc, vc, qf, oacc, mrow, lrow, BLK - 1);
     j = jn;
   };
   // every block before the diagonal, two per trip so that each stage's LDS
@@ -668,13 +705,13 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     __builtin_amdgcn_s_barrier();
     if (slot ? selB : selA) {
       if (odd)
-        pair_tile<D, BLK, true>(cx, lds_k1, lds_v1, qf, oacc, mrow, lrow);
+        pair_tile<D, BLK, true>(cx, lds_k1, lds_v1, qf, oacc, mrow, lrow, klim);
       else
-        pair_tile<D, BLK, true>(cx, lds_k0, lds_v0, qf, oacc, mrow, lrow);
+        pair_tile<D, BLK, true>(cx, lds_k0, lds_v0, qf, oacc, mrow, lrow, klim);
     }
   }
 
-  if (!active) return;
+  if (!active || x >= L) return;
   const float ltot = lrow + __shfl_xor(lrow, 32);
   const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
   uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
@@ -708,7 +745,7 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
                                                        const int32_t* __restrict__ row_count,
                                                        const int32_t* __restrict__ col_idx,
                                                        float* __restrict__ out, int Hq, int Hkv, int nb,
-                                                       int causal, float cscale) {
+                                                       int causal, float cscale, int L) {
   extern __shared__ float smem[];
   float* ks = smem;             // [BLK][D]
   float* vs = smem + BLK * D;   // [BLK][D]
@@ -720,7 +757,7 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
   float qv[D], o[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qv[e] = q[((size_t)x * Hq + h) * D + e] * cscale;
+    qv[e] = x < L ? q[((size_t)x * Hq + h) * D + e] * cscale : 0.0f;
     o[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
@@ -732,12 +769,13 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
     __syncthreads();
     for (int n = threadIdx.x; n < BLK * D; n += BLK) {
       const int r = n / D, e = n % D;
+      const bool in = j * BLK + r < L;  // a short last block ends at L
       const size_t src = ((size_t)(j * BLK + r) * Hkv + g) * D + e;
-      ks[n] = k[src];
-      vs[n] = v[src];
+      ks[n] = in ? k[src] : 0.0f;
+      vs[n] = in ? v[src] : 0.0f;
     }
     __syncthreads();
-    const int ylast = (causal && j == i) ? qr : BLK - 1;
+    const int ylast = min((causal && j == i) ? qr : BLK - 1, L - 1 - j * BLK);
     for (int y = 0; y <= ylast; ++y) {
       float s = 0.0f;
 #pragma unroll
@@ -756,6 +794,7 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
     }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (x >= L) return;
 #pragma unroll
   for (int e = 0; e < D; ++e) out[((size_t)x * Hq + h) * D + e] = o[e] * inv;
 }
@@ -766,10 +805,10 @@ hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStr
   const dim3 grid((unsigned)(g.Hkv * g.nb));
   const __bf16* vv = static_cast<const __bf16*>(v);
   __bf16* out = static_cast<__bf16*>(vt);
-  if (g.d == 128 && g.B == 128) transpose_v_kernel<128, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb);
-  else if (g.d == 128 && g.B == 64) transpose_v_kernel<128, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb);
-  else if (g.d == 64 && g.B == 128) transpose_v_kernel<64, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb);
-  else transpose_v_kernel<64, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb);
+  if (g.d == 128 && g.B == 128) transpose_v_kernel<128, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
+  else if (g.d == 128 && g.B == 64) transpose_v_kernel<128, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
+  else if (g.d == 64 && g.B == 128) transpose_v_kernel<64, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
+  else transpose_v_kernel<64, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
   return hipGetLastError();
 }
 
@@ -786,7 +825,7 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
 #define RR_ATTN_CASE(DV, BV)                                                                      \
   if (g.d == DV && g.B == BV) {                                                                   \
     attn_bf16_kernel<DV, BV><<<grid, BV * 2, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq,    \
-                                                      g.Hkv, g.nb, g.causal, cscale);            \
+                                                      g.Hkv, g.nb, g.causal, cscale, g.L);       \
     return hipGetLastError();                                                                     \
   }
     const int G = g.Hq / g.Hkv;
@@ -794,10 +833,10 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
       const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
       if (g.d == 128)
         attn_bf16_pair_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                              g.nb, g.causal, cscale);
+                                                              g.nb, g.causal, cscale, g.L);
       else
         attn_bf16_pair_kernel<64, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                             g.nb, g.causal, cscale);
+                                                             g.nb, g.causal, cscale, g.L);
       return hipGetLastError();
     }
     RR_ATTN_CASE(128, 128)
@@ -818,7 +857,7 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
     if (fe != hipSuccess) return fe;                                                              \
     attn_f32_kernel<DV, BV><<<grid, BV, lds, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
-                                                   g.nb, g.causal, cscale);                     \
+                                                   g.nb, g.causal, cscale, g.L);                \
     return hipGetLastError();                                                                     \
   }
   RR_F32_CASE(128, 128)

@@ -1,5 +1,6 @@
 // Mass recall of a block selection against full attention: for every row
-// (head h, query block i), the mean over the row's B queries of the share of
+// (head h, query block i), the mean over the row's queries (B, or fewer in a
+// short last block) of the share of
 // each query's full-attention softmax mass that lies on keys of the row's
 // selected blocks. This puts a number on what the Figure 4 and Figure 5
 // captions of "RRAttention: Dynamic Block Sparse Attention via Per-Head
@@ -63,9 +64,11 @@ __device__ __forceinline__ void recall_copy(__amdgpu_buffer_rsrc_t rsrc, uint32_
 }
 
 // One key block for one wave: scores, running maximum, and the two sums.
+// masked: keys with index > klim inside the block are masked (the causal
+// diagonal block: the lane's query row; a short last block: its last key).
 template <int D, int BLK>
 __device__ __forceinline__ void recall_tile(const uint8_t* lds_k, int kro, const bf16x8 (&qf)[D / 16], int half,
-                                            int qr, bool diag, bool sel, float cscale, float& m, float& lall,
+                                            int klim, bool masked, bool sel, float cscale, float& m, float& lall,
                                             float& lsel) {
   typedef RecallCfg<D, BLK> C;
   f32x16 sacc[C::MT];
@@ -79,12 +82,12 @@ __device__ __forceinline__ void recall_tile(const uint8_t* lds_k, int kro, const
     }
     sacc[mt] = acc;
   }
-  if (diag) {
+  if (masked) {
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        if (mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3) > qr) sacc[mt][v] = -INFINITY;
+        if (mt * 32 + 8 * (v >> 2) + 4 * half + (v & 3) > klim) sacc[mt][v] = -INFINITY;
   }
   float tmax = -INFINITY;
 #pragma unroll
@@ -133,7 +136,7 @@ __global__ void __launch_bounds__(BLK * 2) recall_bf16_kernel(const __bf16* __re
                                                                const int32_t* __restrict__ row_count,
                                                                const int32_t* __restrict__ col_idx,
                                                                float* __restrict__ recall, int Hq, int Hkv, int nb,
-                                                               int causal, float cscale) {
+                                                               int causal, float cscale, int L) {
   typedef RecallCfg<D, BLK> C;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[C::TILE];
@@ -151,10 +154,13 @@ __global__ void __launch_bounds__(BLK * 2) recall_bf16_kernel(const __bf16* __re
   const int x = i * BLK + qr;
 
   bf16x8 qf[C::DK];
-  {
+  if (x < L) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
 #pragma unroll
     for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + half];
+  } else {  // past the end of a short last block: not counted
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
   }
   const int kr = tid / C::KCH, kc = (tid % C::KCH) ^ (kr & (C::KCH - 1));
   const uint32_t koff = (uint32_t)((kr * Hkv * D + kc * 8) * 2);
@@ -163,11 +169,16 @@ __global__ void __launch_bounds__(BLK * 2) recall_bf16_kernel(const __bf16* __re
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
   const size_t kstride = (size_t)BLK * Hkv * D * 2;
   const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+  const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
   auto copy = [&](int j, uint8_t* dst) {
+    // cut where the tensor ends: a short last block reads zeros past L
+    const size_t start = (size_t)g * D * 2 + (size_t)j * kstride;
+    const uint32_t kb = start + kbytes <= k_bytes ? kbytes : (uint32_t)(k_bytes - start);
     recall_copy<D, BLK>(__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(kg + (size_t)j * kstride), 0,
-                                                          (int)kbytes, 0x00020000),
+                                                          (int)kb, 0x00020000),
                         koff, kstep, wave, dst);
   };
+  const int ltail = L - (nb - 1) * BLK;  // keys in the last block
 
   const size_t row = (size_t)h * nb + i;
   const int cnt = min(max(row_count[row], 0), nb);
@@ -188,7 +199,8 @@ __global__ void __launch_bounds__(BLK * 2) recall_bf16_kernel(const __bf16* __re
       sel = true;
       ++c;
     }
-    recall_tile<D, BLK>(kc_, kro, qf, half, qr, causal && j == i, sel, cscale, m, lall, lsel);
+    const bool diag = causal && j == i, shortblk = j == nb - 1 && ltail < BLK;
+    recall_tile<D, BLK>(kc_, kro, qf, half, diag ? qr : ltail - 1, diag || shortblk, sel, cscale, m, lall, lsel);
   };
   for (int j = 0; j <= jlast; j += 2) {
     step(j, lds_k0, lds_k1);
@@ -196,8 +208,9 @@ __global__ void __launch_bounds__(BLK * 2) recall_bf16_kernel(const __bf16* __re
   }
   const float ta = lall + __shfl_xor(lall, 32);
   const float ts = lsel + __shfl_xor(lsel, 32);
-  const float r = half == 0 ? ts / ta : 0.0f;  // lanes 32..63 hold the same queries
-  block_mean<C::NW>(r, lane, wave, red, recall + row, 1.0f / BLK);
+  // lanes 32..63 hold the same queries; queries past L are not counted
+  const float r = (half == 0 && x < L) ? ts / ta : 0.0f;
+  block_mean<C::NW>(r, lane, wave, red, recall + row, 1.0f / (float)min(BLK, L - i * BLK));
 }
 
 // float32: thread = query; the key tile of each candidate block in LDS.
@@ -206,7 +219,7 @@ __global__ void __launch_bounds__(BLK) recall_f32_kernel(const float* __restrict
                                                          const int32_t* __restrict__ row_count,
                                                          const int32_t* __restrict__ col_idx,
                                                          float* __restrict__ recall, int Hq, int Hkv, int nb,
-                                                         int causal, float cscale) {
+                                                         int causal, float cscale, int L) {
   __shared__ float ks[BLK * D];
   __shared__ float red[BLK / 64 > 0 ? BLK / 64 : 1];
   const int h = blockIdx.x % Hq;
@@ -216,7 +229,7 @@ __global__ void __launch_bounds__(BLK) recall_f32_kernel(const float* __restrict
   const int x = i * BLK + qr;
   float qv[D];
 #pragma unroll
-  for (int e = 0; e < D; ++e) qv[e] = q[((size_t)x * Hq + h) * D + e] * cscale;
+  for (int e = 0; e < D; ++e) qv[e] = x < L ? q[((size_t)x * Hq + h) * D + e] * cscale : 0.0f;
   const size_t row = (size_t)h * nb + i;
   const int cnt = min(max(row_count[row], 0), nb);
   const int32_t* lst = col_idx + row * nb;
@@ -232,10 +245,10 @@ __global__ void __launch_bounds__(BLK) recall_f32_kernel(const float* __restrict
     __syncthreads();
     for (int n = threadIdx.x; n < BLK * D; n += BLK) {
       const int r = n / D, e = n % D;
-      ks[n] = k[((size_t)(j * BLK + r) * Hkv + g) * D + e];
+      ks[n] = j * BLK + r < L ? k[((size_t)(j * BLK + r) * Hkv + g) * D + e] : 0.0f;
     }
     __syncthreads();
-    const int ylast = (causal && j == i) ? qr : BLK - 1;
+    const int ylast = min((causal && j == i) ? qr : BLK - 1, L - 1 - j * BLK);
     for (int y = 0; y <= ylast; ++y) {
       float s = 0.0f;
 #pragma unroll
@@ -252,7 +265,7 @@ __global__ void __launch_bounds__(BLK) recall_f32_kernel(const float* __restrict
     }
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float r = lsel / lall;
+  float r = x < L ? lsel / lall : 0.0f;  // queries past L are not counted
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) r += __shfl_xor(r, o);
   if (lane == 0) red[wave] = r;
@@ -260,7 +273,7 @@ __global__ void __launch_bounds__(BLK) recall_f32_kernel(const float* __restrict
   if (threadIdx.x == 0) {
     float t = 0.0f;
     for (int w = 0; w < BLK / 64; ++w) t += red[w];
-    recall[row] = t * (1.0f / BLK);
+    recall[row] = t / (float)min(BLK, L - i * BLK);
   }
 }
 
@@ -276,11 +289,11 @@ hipError_t launch_recall(const Geometry& g, const void* q, const void* k, const 
       recall_bf16_kernel<DV, BV><<<grid, BV * 2, 0, st>>>(static_cast<const __bf16*>(q),               \
                                                           static_cast<const __bf16*>(k), row_count,     \
                                                           col_idx, recall, g.Hq, g.Hkv, g.nb, g.causal, \
-                                                          cscale);                                      \
+                                                          cscale, g.L);                                 \
     else                                                                                                \
       recall_f32_kernel<DV, BV><<<grid, BV, 0, st>>>(static_cast<const float*>(q),                     \
                                                      static_cast<const float*>(k), row_count, col_idx,  \
-                                                     recall, g.Hq, g.Hkv, g.nb, g.causal, cscale);      \
+                                                     recall, g.Hq, g.Hkv, g.nb, g.causal, cscale, g.L); \
     return hipGetLastError();                                                                           \
   }
   RR_RECALL_CASE(128, 128)

@@ -24,7 +24,7 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
   if (p->L <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->d <= 0 || p->S <= 0 || p->B <= 0)
     return RR_ERR_INVALID_ARG;
   if (p->Hq % p->Hkv != 0) return RR_ERR_INVALID_ARG;
-  if (p->B % p->S != 0 || p->L % p->B != 0) return RR_ERR_INVALID_ARG;
+  if (p->B % p->S != 0) return RR_ERR_INVALID_ARG;  // L need not be a multiple of B or S
   if (!(p->tau > 0.0f && p->tau <= 1.0f)) return RR_ERR_INVALID_ARG;  // NaN fails too
   if (p->causal != 0 && p->causal != 1) return RR_ERR_INVALID_ARG;
   if (p->dtype != RR_BF16 && p->dtype != RR_FP32) return RR_ERR_INVALID_ARG;
@@ -32,7 +32,7 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
   if (p->B != 64 && p->B != 128) return RR_ERR_UNSUPPORTED;
   const int r = p->B / p->S;
   if (!is_pow2(p->S) || r < 2 || r > 32) return RR_ERR_UNSUPPORTED;
-  const int nb = p->L / p->B;
+  const int nb = (p->L + p->B - 1) / p->B;  // the last block may be short
   if (nb > rr::kMaxSelectBlocks) return RR_ERR_UNSUPPORTED;
   if ((long long)p->Hq * nb > (1LL << 30)) return RR_ERR_UNSUPPORTED;
   g->L = p->L;
@@ -42,7 +42,7 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
   g->S = p->S;
   g->B = p->B;
   g->nb = nb;
-  g->ns = p->L / p->S;
+  g->ns = (p->L + p->S - 1) / p->S;  // the last stride may be short
   g->r = r;
   g->G = p->Hq / p->Hkv;
   g->causal = p->causal;
@@ -63,8 +63,8 @@ Workspace layout(const rr::Geometry& g) {
   off += align_up((size_t)g.ns * g.Hkv * g.d * esz);
   w.mass = off;
   off += align_up((size_t)g.Hq * g.nb * g.nb * sizeof(float));
-  w.vt = off;
-  if (g.bf16) off += align_up((size_t)g.L * g.Hkv * g.d * esz);
+  w.vt = off;  // nb whole tiles: a short last block is padded with zeros
+  if (g.bf16) off += align_up((size_t)g.nb * g.B * g.Hkv * g.d * esz);
   w.total = off;
   return w;
 }
@@ -77,14 +77,14 @@ rr_status check_ws(const rr::Geometry& g, const void* ws, size_t ws_bytes) {
 rr_status hip_status(hipError_t e) { return e == hipSuccess ? RR_OK : RR_ERR_HIP; }
 
 rr_status run_search(const rr::Geometry& g, const void* q, const void* k, int32_t* row_count,
-                     int32_t* col_idx, float* block_mass, void* ws, hipStream_t st) {
+                     int32_t* col_idx, float* block_mass, const float* tau_heads, void* ws, hipStream_t st) {
   const Workspace w = layout(g);
   uint8_t* base = static_cast<uint8_t*>(ws);
   void* kbar = base + w.kbar;
   float* mass = block_mass ? block_mass : reinterpret_cast<float*>(base + w.mass);
   hipError_t e = rr::launch_pool_keys(g, k, kbar, st);
   if (e == hipSuccess) e = rr::launch_search(g, q, kbar, mass, st);
-  if (e == hipSuccess) e = rr::launch_select(g, mass, block_mass != nullptr, row_count, col_idx, st);
+  if (e == hipSuccess) e = rr::launch_select(g, mass, block_mass != nullptr, row_count, col_idx, tau_heads, st);
   return hip_status(e);
 }
 
@@ -120,7 +120,22 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k, i
     return RR_ERR_INVALID_ARG;
   if (block_mass && !aligned16(block_mass)) return RR_ERR_INVALID_ARG;
   if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
-  return run_search(g, q, k, row_count, col_idx, block_mass, ws, static_cast<hipStream_t>(stream));
+  return run_search(g, q, k, row_count, col_idx, block_mass, nullptr, ws, static_cast<hipStream_t>(stream));
+}
+
+rr_status rr_pattern_search_heads(const rr_problem* p, const void* q, const void* k, const float* tau_per_head,
+                                  int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !tau_per_head || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(row_count) || !aligned16(col_idx) ||
+      (reinterpret_cast<uintptr_t>(tau_per_head) & 3u) != 0)
+    return RR_ERR_INVALID_ARG;
+  if (block_mass && !aligned16(block_mass)) return RR_ERR_INVALID_ARG;
+  if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
+  return run_search(g, q, k, row_count, col_idx, block_mass, tau_per_head, ws, static_cast<hipStream_t>(stream));
 }
 
 rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
@@ -148,9 +163,79 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
     return RR_ERR_INVALID_ARG;
   if ((s = check_ws(g, ws, ws_bytes)) != RR_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = run_search(g, q, k, row_count, col_idx, nullptr, ws, st);
+  s = run_search(g, q, k, row_count, col_idx, nullptr, nullptr, ws, st);
   if (s != RR_OK) return s;
   return run_attention(g, q, k, v, row_count, col_idx, out, ws, st);
+}
+
+// Packed variable-length batch: the per-sequence problems, validated before
+// anything is enqueued.
+static rr_status varlen_geometries(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens,
+                                   size_t* ws_max) {
+  if (!p || n_seq <= 0 || !seq_lens) return RR_ERR_INVALID_ARG;
+  long long total = 0;
+  size_t need = 0;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    if (seq_lens[b] <= 0) return RR_ERR_INVALID_ARG;
+    rr_problem pb = *p;
+    pb.L = seq_lens[b];
+    rr::Geometry g;
+    const rr_status s = make_geometry(&pb, &g);
+    if (s != RR_OK) return s;
+    const size_t w = layout(g).total;
+    if (w > need) need = w;
+    total += seq_lens[b];
+  }
+  if (total != p->L) return RR_ERR_INVALID_ARG;
+  *ws_max = need;
+  return RR_OK;
+}
+
+size_t rr_workspace_bytes_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens) {
+  size_t need = 0;
+  return varlen_geometries(p, n_seq, seq_lens, &need) == RR_OK ? need : 0;
+}
+
+rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens, const void* q,
+                            const void* k, const void* v, void* out, int32_t* row_count, int32_t* col_idx,
+                            void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  rr_status s = varlen_geometries(p, n_seq, seq_lens, &need);
+  if (s != RR_OK) return s;
+  if (!q || !k || !v || !out || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(row_count) ||
+      !aligned16(col_idx))
+    return RR_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < need) return RR_ERR_WORKSPACE;
+  // every sequence's tensors and lists must start 16-byte aligned
+  const size_t esz = p->dtype == RR_BF16 ? 2 : 4;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    const size_t nb = ((size_t)seq_lens[b] + p->B - 1) / p->B;
+    if (((size_t)seq_lens[b] * p->Hkv * p->d * esz) % 16 || ((size_t)p->Hq * nb * sizeof(int32_t)) % 16)
+      return RR_ERR_UNSUPPORTED;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  size_t tok = 0, rc_off = 0, ci_off = 0;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    rr_problem pb = *p;
+    pb.L = seq_lens[b];
+    rr::Geometry g;
+    make_geometry(&pb, &g);
+    const uint8_t* qb = static_cast<const uint8_t*>(q) + tok * p->Hq * p->d * esz;
+    const uint8_t* kb = static_cast<const uint8_t*>(k) + tok * p->Hkv * p->d * esz;
+    const uint8_t* vb = static_cast<const uint8_t*>(v) + tok * p->Hkv * p->d * esz;
+    uint8_t* ob = static_cast<uint8_t*>(out) + tok * p->Hq * p->d * esz;
+    int32_t* rcb = row_count + rc_off;
+    int32_t* cib = col_idx + ci_off;
+    s = run_search(g, qb, kb, rcb, cib, nullptr, nullptr, ws, st);
+    if (s != RR_OK) return s;
+    s = run_attention(g, qb, kb, vb, rcb, cib, ob, ws, st);
+    if (s != RR_OK) return s;
+    tok += seq_lens[b];
+    rc_off += (size_t)g.Hq * g.nb;
+    ci_off += (size_t)g.Hq * g.nb * g.nb;
+  }
+  return RR_OK;
 }
 
 rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, const int32_t* row_count,

@@ -11,7 +11,7 @@ namespace rr {
 // Geometry shared by the launches of one problem.
 struct Geometry {
   int L, Hq, Hkv, d, S, B;
-  int nb, ns, r, G;
+  int nb, ns, r, G;  // nb = ceil(L / B), ns = ceil(L / S): the last block and stride may be short
   int causal;
   int bf16;  // 1: bfloat16 tensors, 0: float32
   float tau;
@@ -21,8 +21,9 @@ struct Geometry {
 hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStream_t st);
 hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, float* mass,
                          hipStream_t st);
+// tau_heads: optional device thresholds [Hq] in place of g.tau.
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
-                         int32_t* col_idx, hipStream_t st);
+                         int32_t* col_idx, const float* tau_heads, hipStream_t st);
 
 // Variant: every head of a KV head gets the union of the group's selections.
 hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,

@@ -9,10 +9,10 @@
 // query block), Figure 2 caption (stride S, block B, three stages).
 //
 // Kernels
-//   pool_keys   K [L][Hkv][d] -> Kbar [L/S][Hkv][d]: float32 sum of the S keys
-//               of a stride in token order, times 1/S (S is a power of two, so
-//               this equals the division), rounded to the input dtype.
-//               HBM stream: reads K once, writes Kbar.
+//   pool_keys   K [L][Hkv][d] -> Kbar [ceil(L/S)][Hkv][d]: float32 sum of the
+//               keys of a stride in token order (S of them, fewer in a short
+//               last stride), divided by their count, rounded to the input
+//               dtype. HBM stream: reads K once, writes Kbar.
 //   search      one workgroup per (query block i < nb-1, KV head g, chunk of
 //               that group's query heads). Sampled query of head h in stride s
 //               is token s*S + (h mod S). Scores are computed transposed,
@@ -54,20 +54,21 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
 
 template <typename T>
 __global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k, T* __restrict__ kbar,
-                                                        int ns, int row_chunks, int S) {
+                                                        int ns, int row_chunks, int S, int L) {
   // one thread per 16-byte chunk of a pooled row; row_chunks = Hkv * d * sizeof(T) / 16
   const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
   if (n >= (long long)ns * row_chunks) return;
   const int t = (int)(n / row_chunks);
   const int c = (int)(n % row_chunks);
   const u32x4* src = reinterpret_cast<const u32x4*>(k) + (size_t)t * S * row_chunks + c;
-  const float inv = 1.0f / (float)S;  // exact: S is a power of two
+  const int cnt = min(S, L - t * S);  // tokens in this stride
+  const float fcnt = (float)cnt;      // a division by it (by S: exact scaling)
   u32x4 res;
   if constexpr (sizeof(T) == 2) {
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    for (int u = 0; u < S; ++u) {
+    for (int u = 0; u < cnt; ++u) {
       const u32x4 w = src[(size_t)u * row_chunks];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -77,16 +78,16 @@ __global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k,
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      res[e] = float_to_bf16_bits(acc[2 * e] * inv) | (float_to_bf16_bits(acc[2 * e + 1] * inv) << 16);
+      res[e] = float_to_bf16_bits(acc[2 * e] / fcnt) | (float_to_bf16_bits(acc[2 * e + 1] / fcnt) << 16);
   } else {
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int u = 0; u < S; ++u) {
+    for (int u = 0; u < cnt; ++u) {
       const u32x4 w = src[(size_t)u * row_chunks];
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) res[e] = __float_as_uint(acc[e] * inv);
+    for (int e = 0; e < 4; ++e) res[e] = __float_as_uint(acc[e] / fcnt);
   }
   reinterpret_cast<u32x4*>(kbar)[n] = res;
 }
@@ -306,7 +307,7 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
 __global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, int zero_fill,
                                                      int32_t* __restrict__ row_count,
                                                      int32_t* __restrict__ col_idx, int nb, int causal,
-                                                     float tau) {
+                                                     float tau_all, const float* __restrict__ tau_heads) {
   extern __shared__ uint64_t keys[];  // np2 sort keys, then np2 int flags
   __shared__ float part[256];
   __shared__ int ipart[256];
@@ -317,6 +318,10 @@ __global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, i
   const int ncand = causal ? i + 1 : nb;
   float* mrow = mass + (size_t)row * nb;
   int32_t* out = col_idx + (size_t)row * nb;
+  // a threshold per query head when given; NaN or values outside (0, 1] keep
+  // every candidate block (never drops mass)
+  float tau = tau_heads ? tau_heads[row / nb] : tau_all;
+  if (!(tau > 0.0f && tau < 1.0f)) tau = 1.0f;
 
   if (zero_fill) {  // exported masses: non-candidates and the unsearched last row are zero
     const int from = (i == nb - 1) ? 0 : ncand;
@@ -502,10 +507,10 @@ hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStr
   const dim3 grid((unsigned)((n + 255) / 256));
   if (g.bf16)
     pool_keys_kernel<__bf16><<<grid, 256, 0, st>>>(static_cast<const __bf16*>(k),
-                                                   static_cast<__bf16*>(kbar), g.ns, row_chunks, g.S);
+                                                   static_cast<__bf16*>(kbar), g.ns, row_chunks, g.S, g.L);
   else
     pool_keys_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(k),
-                                                  static_cast<float*>(kbar), g.ns, row_chunks, g.S);
+                                                  static_cast<float*>(kbar), g.ns, row_chunks, g.S, g.L);
   return hipGetLastError();
 }
 
@@ -518,7 +523,7 @@ hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, flo
 }
 
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
-                         int32_t* col_idx, hipStream_t st) {
+                         int32_t* col_idx, const float* tau_heads, hipStream_t st) {
   int np2 = 1;
   while (np2 < g.nb) np2 <<= 1;
   const size_t lds = (size_t)np2 * (sizeof(uint64_t) + sizeof(int));
@@ -527,7 +532,7 @@ hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, in
   if (e != hipSuccess) return e;
   select_kernel<<<dim3((unsigned)(g.Hq * g.nb)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill,
                                                                  row_count, col_idx, g.nb, g.causal,
-                                                                 g.tau);
+                                                                 g.tau, tau_heads);
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@
  *     row-major and contiguous, in the dtype named by the problem (bfloat16
  *     or float32). Query head h uses KV head h / (Hq / Hkv) (grouped-query
  *     attention with consecutive grouping).
- *   - nb = L / B query (and key) blocks. Block lists: row_count is int32
+ *   - nb = ceil(L / B) query (and key) blocks; when B does not divide L the
+ *     last block is short (L - (nb - 1) B tokens), and likewise the last
+ *     stride of S tokens (its pooled key is the mean of the keys it has).
+ *     Block lists: row_count is int32
  *     [Hq][nb], col_idx is int32 [Hq][nb][nb]; row (h, i) selects key blocks
  *     col_idx[h][i][0 .. row_count[h][i]) in strictly ascending order; the
  *     remaining entries are unspecified.
@@ -36,9 +39,9 @@
  *     the ABI.
  *
  * Supported problems: dtype bf16 or fp32; d in {64, 128}; B in {64, 128};
- * S a power of two with r = B / S in {2, 4, 8, 16, 32}; L a multiple of B;
- * Hq a multiple of Hkv; 0 < tau <= 1 (tau = 1 keeps every candidate block);
- * causal 0 or 1.
+ * S a power of two with r = B / S in {2, 4, 8, 16, 32}; any L >= 1 with
+ * ceil(L / B) <= 8192; Hq a multiple of Hkv; 0 < tau <= 1 (tau = 1 keeps every
+ * candidate block); causal 0 or 1.
  */
 #ifndef RR_ATTN_H
 #define RR_ATTN_H
@@ -111,6 +114,17 @@ rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k
                                const int32_t* row_count, const int32_t* col_idx, void* out,
                                void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Stage 1 with a threshold per query head (a serving extension; the pages use
+ * one tau): tau_per_head is a DEVICE float array [Hq]; head h keeps the
+ * blocks of its rows up to tau_per_head[h] of the row total. A value that is
+ * NaN or outside (0, 1] keeps every candidate block. p->tau must still be
+ * valid and is not used. Other arguments as rr_pattern_search.
+ */
+rr_status rr_pattern_search_heads(const rr_problem* p, const void* q, const void* k, const float* tau_per_head,
+                                  int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Both stages back to back on one stream: search, then attention over the
  * lists it produced (row_count / col_idx are outputs, as in stage 1). */
 rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const void* v, void* out,
@@ -150,6 +164,24 @@ rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, cons
  */
 rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, const int32_t* col_idx,
                                int32_t* shared_row_count, int32_t* shared_col_idx, void* stream);
+
+/*
+ * A batch of independent sequences of different lengths packed along the
+ * token axis, without padding (varlen prefill). p describes every sequence
+ * except its length: p->L must equal the sum of the n_seq lengths in
+ * seq_lens (a HOST array, each entry >= 1; a length need not be a multiple
+ * of B). q, k, v and out are the packed tensors ([sum L_b][H][d]). The lists
+ * of sequence b follow those of the sequences before it: row_count at entry
+ * offset sum_{b'<b} Hq nb_b', col_idx at sum_{b'<b} Hq nb_b'^2, with
+ * nb_b = ceil(L_b / B). Every sequence's slices must stay 16-byte aligned
+ * (else RR_ERR_UNSUPPORTED). The sequences run one after the other on the
+ * stream, sharing one workspace of rr_workspace_bytes_varlen bytes (0 for an
+ * invalid batch). All lengths are checked before anything is enqueued.
+ */
+size_t rr_workspace_bytes_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens);
+rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens, const void* q,
+                            const void* k, const void* v, void* out, int32_t* row_count, int32_t* col_idx,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* rr_status_string(rr_status s);

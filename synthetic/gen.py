@@ -56,11 +56,11 @@ class Workload:
 
     @property
     def nb(self) -> int:
-        return self.L // self.B
+        return -(-self.L // self.B)
 
     @property
     def ns(self) -> int:
-        return self.L // self.S
+        return -(-self.L // self.S)
 
     @property
     def G(self) -> int:

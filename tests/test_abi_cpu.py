@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
                             "rr_prefill", "rr_mass_recall", "rr_share_group_lists", "rr_status_string",
-                            "rr_version"])
+                            "rr_version", "rr_pattern_search_heads", "rr_workspace_bytes_varlen",
+                            "rr_prefill_varlen"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -51,12 +52,16 @@ def test_workspace_bytes():
     # pooled keys + block masses + key-major V copy, each 256-byte aligned
     assert n == ns * 8 * 128 * 2 + 32 * nb * nb * 4 + 16384 * 8 * 128 * 2
     assert rr.rr_workspace_bytes(base(dtype=rr.RR_FP32)) == ns * 8 * 128 * 4 + 32 * nb * nb * 4
+    # a ragged length: ceil(L / B) blocks, ceil(L / S) strides, V copy padded to whole blocks
+    n = rr.rr_workspace_bytes(base(L=1000))
+    al = lambda x: -(-x // 256) * 256
+    assert n == al(63 * 8 * 128 * 2) + al(32 * 8 * 8 * 4) + al(8 * 128 * 8 * 128 * 2)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(L=0), rr.RR_ERR_INVALID_ARG),
     (dict(Hq=30), rr.RR_ERR_INVALID_ARG),           # not a multiple of Hkv
-    (dict(L=1000), rr.RR_ERR_INVALID_ARG),          # not a multiple of B
+    (dict(S=48), rr.RR_ERR_INVALID_ARG),            # B not a multiple of S
     (dict(S=48), rr.RR_ERR_INVALID_ARG),            # B not a multiple of S
     (dict(tau=0.0), rr.RR_ERR_INVALID_ARG),
     (dict(tau=1.5), rr.RR_ERR_INVALID_ARG),
@@ -119,3 +124,33 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros((256, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         rr.rr_pattern_search(p, q, q, q, q, None, q, stream=0)
+
+
+def test_varlen_and_per_head_checks_on_host():
+    lib = rr.load()
+    ok = 1 << 20
+    p = base(L=300 + 1000 + 128)
+    lens = (ctypes.c_int32 * 3)(300, 1000, 128)
+    need = lib.rr_workspace_bytes_varlen(ctypes.byref(p), 3, lens)
+    # the largest single sequence decides
+    assert need == rr.rr_workspace_bytes(base(L=1000))
+    # lengths must add up to p->L, be positive, and be given
+    bad = base(L=1427)
+    assert lib.rr_workspace_bytes_varlen(ctypes.byref(bad), 3, lens) == 0
+    assert lib.rr_prefill_varlen(ctypes.byref(bad), 3, lens, ok, ok, ok, ok, ok, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    zero = (ctypes.c_int32 * 2)(0, 1428)
+    assert lib.rr_prefill_varlen(ctypes.byref(p), 2, zero, ok, ok, ok, ok, ok, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_prefill_varlen(ctypes.byref(p), 3, None, ok, ok, ok, ok, ok, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_prefill_varlen(ctypes.byref(p), 3, lens, ok, ok, ok, ok, ok, ok, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
+    assert rr.rr_workspace_bytes_varlen(p, [300, 1000, 128]) == need
+    # the next sequence's lists would start misaligned: Hq * nb * 4 bytes is not a multiple of 16
+    small = rr.Problem(128, 2, 2, 64, 8, 64, 0.9, 1, rr.RR_BF16)
+    two = (ctypes.c_int32 * 2)(64, 64)
+    w2 = lib.rr_workspace_bytes_varlen(ctypes.byref(small), 2, two)
+    assert w2 > 0
+    assert lib.rr_prefill_varlen(ctypes.byref(small), 2, two, ok, ok, ok, ok, ok, ok, ok, w2, 0) == rr.RR_ERR_UNSUPPORTED
+    # per-head thresholds: null array, misaligned array
+    q = base()
+    w = rr.rr_workspace_bytes(q)
+    assert lib.rr_pattern_search_heads(ctypes.byref(q), ok, ok, None, ok, ok, None, ok, w, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_pattern_search_heads(ctypes.byref(q), ok, ok, ok + 2, ok, ok, None, ok, w, 0) == rr.RR_ERR_INVALID_ARG
