@@ -122,6 +122,76 @@ def cpu_baseline(w, q, k, v, rc, ci, f_comp, seconds_hint=20.0):
     }
 
 
+# ragged sequence lengths of the packed batch (none a multiple of B = 128), 131,072 tokens in all
+VARLEN_LENS = [40000, 23456, 17000, 16383, 12800, 9999, 6000, 5434]
+
+
+def bench_varlen(args):
+    """Packed batch of sequences (rr_prefill_varlen); one JSON line like the single-sequence bench."""
+    import torch
+
+    import dynamic_block_sparse_rr_amd as rr
+    from synthetic.gen import Workload, make_inputs
+
+    lens = VARLEN_LENS
+    assert sum(lens) == 131072
+    tau = args.tau if args.tau is not None else 0.9
+    parts = [make_inputs(Workload("llama8b_seq%d" % b, L, 32, 8, 128, "bf16", 128, 16, (tau,), 40 + b, "llm", 64))
+             for b, L in enumerate(lens)]
+    q = torch.cat([x[0] for x in parts]).cuda()
+    k = torch.cat([x[1] for x in parts]).cuda()
+    v = torch.cat([x[2] for x in parts]).cuda()
+    del parts
+    p = rr.problem(sum(lens), 32, 8, 128, 16, 128, tau, True, "bf16")
+    nbs = [-(-L // 128) for L in lens]
+    rc = torch.empty((sum(32 * n for n in nbs),), dtype=torch.int32, device="cuda")
+    ci = torch.empty((sum(32 * n * n for n in nbs),), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(rr.rr_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rr.rr_prefill_varlen(p, lens, q, k, v, out, rc, ci, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        step()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    rcn, cin = rc.cpu().numpy(), ci.cpu().numpy()
+    f_comp = 0.0
+    blocks = cand = 0
+    roff = coff = 0
+    for L, nb in zip(lens, nbs):
+        rcb = rcn[roff:roff + 32 * nb].reshape(32, nb)
+        cib = cin[coff:coff + 32 * nb * nb].reshape(32, nb, nb)
+        f, nblk, _ = computed_flops(rcb, cib, 128, 128, True)
+        f_comp += f
+        blocks += nblk
+        cand += 32 * nb * (nb + 1) // 2
+        roff += 32 * nb
+        coff += 32 * nb * nb
+    value = f_comp / (ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama8b_varlen_batch_128k", "seq_lens": lens, "Hq": 32, "Hkv": 8, "d": 128,
+                   "B": 128, "S": 16, "tau": tau, "causal": True},
+        "step_ms_median_events": round(float(np.median(ev_ms)), 3),
+        "blocks_computed_pct": round(100.0 * blocks / cand, 2),
+        "note": "search + attention of every sequence, one after the other on one stream (rr_prefill_varlen)",
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +207,9 @@ def main():
     ap.add_argument("--shared-mask", action="store_true",
                     help="variant: every head of a KV head attends over the union of the group's selections "
                          "(rr_share_group_lists runs inside the step, after the search)")
+    ap.add_argument("--varlen", action="store_true",
+                    help="a packed batch of LLaMA-8B-shaped sequences of ragged lengths (about 128K tokens in "
+                         "all) through rr_prefill_varlen instead of one sequence")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
                          "reported as cold_* fields, events only")
@@ -154,6 +227,8 @@ def main():
     import dynamic_block_sparse_rr_amd as rr
     from synthetic.gen import make_inputs, workload
 
+    if args.varlen:
+        return bench_varlen(args)
     w = workload(args.workload)
     tau = args.tau if args.tau is not None else w.taus[len(w.taus) // 2]
     log(f"workload {w.name}: L={w.L} Hq={w.Hq} Hkv={w.Hkv} d={w.d} B={w.B} S={w.S} tau={tau}")
