@@ -74,6 +74,8 @@ def _load():
         lib.rro_recall.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, ctypes.c_longlong, P,
                                    ctypes.c_int]
         lib.rro_recall.restype = ctypes.c_int
+        lib.rro_decode.argtypes = [ctypes.POINTER(_Problem), P, P, P, P, P, P, P, ctypes.c_int]
+        lib.rro_decode.restype = ctypes.c_int
         lib.rro_max_threads.argtypes = []
         lib.rro_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -261,6 +263,37 @@ def share_group_lists(row_count, col_idx, G: int):
                 out_rc[h, i] = len(js)
                 out_ci[h, i, : len(js)] = js
     return out_rc, out_ci
+
+
+@dataclass
+class DecodeResult:
+    row_count: np.ndarray  # int32 [Hq]
+    col_idx: np.ndarray    # int32 [Hq][nb], -1 padded
+    mass: np.ndarray       # float32 [Hq][nb]
+    out: np.ndarray        # float64 [Hq][d]
+
+
+def decode(q, k, v, *, S: int, B: int, tau: float, round_bf16: bool, nthreads: int = 0) -> DecodeResult:
+    """One decode step: the new query q [Hq][d] against the cache k, v [L][Hkv][d]
+    (its own key and value at position L - 1). Block masses of the query's
+    stride softmax, the Top-tau prefix plus the last block, then attention over
+    the selected blocks in float64."""
+    q = _f32(q)
+    k = _f32(k)
+    v = _f32(v)
+    L, Hkv, d = k.shape
+    Hq = q.shape[0]
+    nb = -(-L // B)
+    p = _problem(L, Hq, Hkv, d, S, B, tau, 1, round_bf16)
+    rc = np.zeros((Hq,), np.int32)
+    ci = np.zeros((Hq, nb), np.int32)
+    mass = np.zeros((Hq, nb), np.float32)
+    out = np.zeros((Hq, d), np.float64)
+    st = _load().rro_decode(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rc), _ptr(ci), _ptr(mass), _ptr(out),
+                            int(nthreads))
+    if st:
+        raise ValueError("rro_decode failed (%d)" % st)
+    return DecodeResult(rc, ci, mass, out)
 
 
 def full_lists(L: int, Hq: int, B: int, causal: bool = True):

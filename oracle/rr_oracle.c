@@ -437,3 +437,121 @@ int rro_recall(const rro_problem* p, const float* Q, const float* K, const int32
   }
   return status;
 }
+
+/*
+ * Decode step (the TL;DR names decode-stage sparsification as future work;
+ * the readings below are the plainest ones the prefill definition supports):
+ * the cache holds L tokens, the new token's own key and value included at
+ * position L - 1, and q[h] is the new query of head h (it sees every cached
+ * key). Block selection reuses the prefill's pieces with the query itself in
+ * place of the round-robin samples:
+ *   scores  z_t = q[h] . Kbar[t][g(h)] / sqrt(d) over every stride t of the
+ *           cache (Kbar as in rro_pool, the last stride possibly short);
+ *   mass    m_j = sum over the strides t of key block j of softmax_t(z);
+ *   select  the Top-tau prefix of the (mass desc, index asc) order, as in
+ *           prefill, plus the last key block (the one holding the query),
+ *           which is always kept; tau >= 1 keeps every block.
+ * Attention: out[h] = softmax over the keys of the selected blocks (y < L)
+ * of q[h] . K[y] / sqrt(d), applied to V; float64, two passes.
+ * Outputs: row_count [Hq], col_idx [Hq][nb] (ascending, tail -1), mass
+ * [Hq][nb] (float32), out [Hq][d] (float64). Search in float32 like prefill.
+ */
+int rro_decode(const rro_problem* p, const float* q, const float* K, const float* V, int32_t* row_count,
+               int32_t* col_idx, float* mass, double* out, int nthreads) {
+  if (check_problem(p) || !q || !K || !V || !row_count || !col_idx || !mass || !out) return 1;
+  const int L = p->L, Hq = p->Hq, Hkv = p->Hkv, d = p->d, B = p->B;
+  const int ns = n_strides(p), nb = n_blocks(p), r = B / p->S, G = Hq / Hkv;
+  const float sigma = 1.0f / sqrtf((float)d);
+  float* Kbar = (float*)malloc(sizeof(float) * (size_t)ns * Hkv * d);
+  if (!Kbar) return 2;
+  rro_pool(p, K, Kbar);
+  int status = 0;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    float* z = (float*)malloc(sizeof(float) * (size_t)ns);
+    mass_idx* order = (mass_idx*)malloc(sizeof(mass_idx) * (size_t)nb);
+    char* keep = (char*)malloc((size_t)nb);
+    double* a = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!z || !order || !keep || !a) {
+#pragma omp atomic write
+      status = 2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int h = 0; h < Hq; ++h) {
+        const int g = h / G;
+        const float* qv = q + (size_t)h * d;
+        float* m = mass + (size_t)h * nb;
+        /* block masses of the query's stride softmax */
+        float mu = -INFINITY;
+        for (int t = 0; t < ns; ++t) {
+          const float* kv = Kbar + ((size_t)t * Hkv + g) * d;
+          float dot = 0.0f;
+          for (int e = 0; e < d; ++e) dot += qv[e] * kv[e];
+          z[t] = sigma * dot;
+          if (z[t] > mu) mu = z[t];
+        }
+        float l = 0.0f;
+        for (int t = 0; t < ns; ++t) l += expf(z[t] - mu);
+        for (int j = 0; j < nb; ++j) m[j] = 0.0f;
+        for (int t = 0; t < ns; ++t) m[t / r] += expf(z[t] - mu) / l;
+        /* Top-tau prefix of the order, plus the last block */
+        for (int j = 0; j < nb; ++j) {
+          order[j].m = m[j];
+          order[j].j = j;
+          keep[j] = 0;
+        }
+        qsort(order, (size_t)nb, sizeof(mass_idx), by_mass_desc);
+        float T = 0.0f;
+        for (int k = 0; k < nb; ++k) T += order[k].m;
+        if (p->tau >= 1.0f) {
+          for (int j = 0; j < nb; ++j) keep[j] = 1;
+        } else {
+          float before = 0.0f;
+          const float thr = p->tau * T;
+          for (int k = 0; k < nb; ++k) {
+            if (before < thr) keep[order[k].j] = 1;
+            before += order[k].m;
+          }
+        }
+        keep[nb - 1] = 1;
+        int cnt = 0;
+        int32_t* lst = col_idx + (size_t)h * nb;
+        for (int j = 0; j < nb; ++j)
+          if (keep[j]) lst[cnt++] = j;
+        for (int j = cnt; j < nb; ++j) lst[j] = -1;
+        row_count[h] = cnt;
+        /* attention over the selected blocks' keys */
+        int ny = 0;
+        double mx = -INFINITY;
+        for (int c = 0; c < cnt; ++c)
+          for (int y = lst[c] * B; y < (lst[c] + 1) * B && y < L; ++y) {
+            const float* kv = K + ((size_t)y * Hkv + g) * d;
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e) dot += (double)qv[e] * (double)kv[e];
+            a[ny] = dot / sqrt((double)d);
+            if (a[ny] > mx) mx = a[ny];
+            ++ny;
+          }
+        double* o = out + (size_t)h * d;
+        for (int e = 0; e < d; ++e) o[e] = 0.0;
+        double lsum = 0.0;
+        int n = 0;
+        for (int c = 0; c < cnt; ++c)
+          for (int y = lst[c] * B; y < (lst[c] + 1) * B && y < L; ++y) {
+            const double w = exp(a[n++] - mx);
+            lsum += w;
+            const float* vv = V + ((size_t)y * Hkv + g) * d;
+            for (int e = 0; e < d; ++e) o[e] += w * (double)vv[e];
+          }
+        for (int e = 0; e < d; ++e) o[e] /= lsum;
+      }
+    }
+    free(z);
+    free(order);
+    free(keep);
+    free(a);
+  }
+  free(Kbar);
+  return status;
+}
