@@ -192,6 +192,74 @@ def bench_varlen(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_decode(args):
+    """One decode step of the 128K layer: the last token's queries against the whole cache."""
+    import torch
+
+    import dynamic_block_sparse_rr_amd as rr
+    from synthetic.gen import make_inputs, workload
+
+    w = workload(args.workload)
+    tau = args.tau if args.tau is not None else w.taus[len(w.taus) // 2]
+    Q, K, V = make_inputs(w)
+    q = Q[w.L - 1].contiguous().cuda()
+    k, v = K.cuda(), V.cuda()
+    del Q
+    stream = torch.cuda.current_stream()
+    res = {}
+    for t in (tau, 1.0):
+        p = rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, t, True, w.dtype)
+        kbar = torch.empty((p.ns, w.Hkv, w.d), dtype=k.dtype, device="cuda")
+        out = torch.empty_like(q)
+        rc = torch.empty((w.Hq,), dtype=torch.int32, device="cuda")
+        ci = torch.empty((w.Hq, w.nb), dtype=torch.int32, device="cuda")
+        ws = torch.empty(rr.rr_decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        rr.rr_pool_keys(p, k, kbar, stream=stream)
+        e[1].record(stream)
+        for _ in range(max(3, args.warmup)):
+            rr.rr_decode(p, q, k, v, out, rc, ci, None, ws, stream=stream, kbar=kbar)
+        n = max(20, 10 * args.steps)
+        e[2].record(stream)
+        for _ in range(n):
+            rr.rr_decode(p, q, k, v, out, rc, ci, None, ws, stream=stream, kbar=kbar)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        us = e[2].elapsed_time(e[3]) * 1e3 / n
+        rcn, cin = rc.cpu().numpy(), ci.cpu().numpy()
+        # algorithmic bytes: K and V of the blocks each KV head's query heads selected (their union),
+        # the pooled keys once, the queries and outputs
+        tile = 2 * w.B * w.d * 2
+        union = 0
+        for g in range(w.Hkv):
+            sel = set()
+            for h in range(g * w.G, (g + 1) * w.G):
+                sel.update(int(j) for j in cin[h, : rcn[h]])
+            union += len(sel)
+        esz = 2 if w.dtype == "bf16" else 4
+        nbytes = union * tile + p.ns * w.Hkv * w.d * esz + 2 * w.Hq * w.d * esz
+        res[t] = {"us": us, "pool_us": e[0].elapsed_time(e[1]) * 1e3, "kept": float(rcn.mean() / w.nb),
+                  "bytes": nbytes, "tbps": nbytes / (us * 1e-6) / 1e12}
+    r, d_ = res[tau], res[1.0]
+    line = {
+        "metric": "decode step us per layer at 128K (one new token, pooled keys kept with the cache)",
+        "value": round(r["us"], 2), "unit": "us", "n_gpus": 1, "steps": max(20, 10 * args.steps),
+        "warmup": max(3, args.warmup), "ms_per_step": round(r["us"] / 1e3, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + "_decode", "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "B": w.B,
+                   "S": w.S, "tau": tau},
+        "blocks_kept": round(r["kept"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(r["tbps"] * 1e3, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(r["tbps"] / 8.0, 4), "traffic": None,
+                     "algorithmic_bytes": r["bytes"]},
+        "dense_decode_us": round(d_["us"], 2), "dense_decode_GBps": round(d_["tbps"] * 1e3, 1),
+        "speedup_vs_dense": round(d_["us"] / r["us"], 3),
+        "pool_keys_us_whole_cache": round(r["pool_us"], 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +278,8 @@ def main():
     ap.add_argument("--varlen", action="store_true",
                     help="a packed batch of LLaMA-8B-shaped sequences of ragged lengths (about 128K tokens in "
                          "all) through rr_prefill_varlen instead of one sequence")
+    ap.add_argument("--decode", action="store_true",
+                    help="one decode step against the 128K cache (rr_decode, pooled keys given) instead of prefill")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
                          "reported as cold_* fields, events only")
@@ -229,6 +299,8 @@ def main():
 
     if args.varlen:
         return bench_varlen(args)
+    if args.decode:
+        return bench_decode(args)
     w = workload(args.workload)
     tau = args.tau if args.tau is not None else w.taus[len(w.taus) // 2]
     log(f"workload {w.name}: L={w.L} Hq={w.Hq} Hkv={w.Hkv} d={w.d} B={w.B} S={w.S} tau={tau}")

@@ -40,6 +40,10 @@ class Problem(ctypes.Structure):
     def nb(self) -> int:
         return -(-self.L // self.B)  # the last block may be short
 
+    @property
+    def ns(self) -> int:
+        return -(-self.L // self.S)  # the last stride may be short
+
     def __repr__(self):
         return ("Problem(L=%d, Hq=%d, Hkv=%d, d=%d, S=%d, B=%d, tau=%g, causal=%d, dtype=%d)"
                 % (self.L, self.Hq, self.Hkv, self.d, self.S, self.B, self.tau, self.causal, self.dtype))
@@ -81,6 +85,12 @@ def load():
         lib.rr_workspace_bytes_varlen.restype = ctypes.c_size_t
         lib.rr_prefill_varlen.argtypes = [PP, ctypes.c_int32, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.rr_prefill_varlen.restype = ctypes.c_int
+        lib.rr_decode_workspace_bytes.argtypes = [PP]
+        lib.rr_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.rr_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_decode.restype = ctypes.c_int
+        lib.rr_pool_keys.argtypes = [PP, P, P, P]
+        lib.rr_pool_keys.restype = ctypes.c_int
         lib.rr_status_string.argtypes = [ctypes.c_int]
         lib.rr_status_string.restype = ctypes.c_char_p
         lib.rr_version.argtypes = []
@@ -189,6 +199,20 @@ def rr_prefill_varlen(p, seq_lens, q, k, v, out, row_count, col_idx, ws, ws_byte
     _check("rr_prefill_varlen", load().rr_prefill_varlen(
         ctypes.byref(p), int(a.size), ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
         _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_decode_workspace_bytes(p: Problem) -> int:
+    return int(load().rr_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def rr_decode(p, q, k, v, out, row_count, col_idx, block_mass, ws, ws_bytes=None, stream=None, kbar=None):
+    _check("rr_decode", load().rr_decode(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), _ptr(out), _ptr(row_count), _ptr(col_idx),
+        _ptr(block_mass), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_pool_keys(p, k, kbar, stream=None):
+    _check("rr_pool_keys", load().rr_pool_keys(ctypes.byref(p), _ptr(k), _ptr(kbar), _stream(stream)))
 
 
 def rr_status_string(status: int) -> str:

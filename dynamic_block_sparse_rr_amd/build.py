@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librr_attn.so")
-SOURCES = ["rr_host.cpp", "search.hip", "attn.hip", "recall.hip"]
+SOURCES = ["rr_host.cpp", "search.hip", "attn.hip", "recall.hip", "decode.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

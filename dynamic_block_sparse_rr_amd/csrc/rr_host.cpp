@@ -270,6 +270,84 @@ rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, co
                                            static_cast<hipStream_t>(stream)));
 }
 
+// Decode workspace: pooled keys | block sums [Hq][nb] | score-chunk partials | masses [Hq][nb] |
+// selection flags [Hq][nbp] | split partials.
+struct DecodeWorkspace {
+  size_t kbar, bsum, zpart, mass, sel, part, total;
+  int nbp;
+};
+
+DecodeWorkspace decode_layout(const rr::Geometry& g) {
+  const size_t esz = g.bf16 ? 2 : 4;
+  DecodeWorkspace w;
+  size_t off = 0;
+  w.kbar = off;
+  off += align_up((size_t)g.ns * g.Hkv * g.d * esz);
+  w.bsum = off;
+  off += align_up((size_t)g.Hq * g.nb * sizeof(float));
+  w.zpart = off;
+  off += align_up((size_t)g.Hq * rr::decode_chunks(g) * 2 * sizeof(float));
+  w.mass = off;
+  off += align_up((size_t)g.Hq * g.nb * sizeof(float));
+  w.sel = off;
+  w.nbp = (g.nb + 15) / 16 * 16;
+  off += align_up((size_t)g.Hq * w.nbp);
+  w.part = off;
+  off += align_up((size_t)g.Hq * rr::decode_splits(g) * (g.d + 2) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+size_t rr_decode_workspace_bytes(const rr_problem* p) {
+  rr::Geometry g;
+  if (make_geometry(p, &g) != RR_OK) return 0;
+  return decode_layout(g).total;
+}
+
+rr_status rr_pool_keys(const rr_problem* p, const void* k, void* kbar, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!k || !kbar || !aligned16(k) || !aligned16(kbar)) return RR_ERR_INVALID_ARG;
+  return hip_status(rr::launch_pool_keys(g, k, kbar, static_cast<hipStream_t>(stream)));
+}
+
+rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar, void* out,
+                    int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
+                    void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !v || !out || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(row_count) ||
+      !aligned16(col_idx))
+    return RR_ERR_INVALID_ARG;
+  if (block_mass && !aligned16(block_mass)) return RR_ERR_INVALID_ARG;
+  if (kbar && !aligned16(kbar)) return RR_ERR_INVALID_ARG;
+  const DecodeWorkspace w = decode_layout(g);
+  if (!ws || !aligned16(ws) || ws_bytes < w.total) return RR_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* mass = block_mass ? block_mass : reinterpret_cast<float*>(base + w.mass);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (!kbar) {  // pool the cache's keys here
+    e = rr::launch_pool_keys(g, k, base + w.kbar, st);
+    kbar = base + w.kbar;
+  }
+  if (e == hipSuccess)
+    e = rr::launch_decode_scores(g, q, kbar, reinterpret_cast<float*>(base + w.bsum),
+                                 reinterpret_cast<float*>(base + w.zpart), st);
+  uint8_t* sel = base + w.sel;
+  if (e == hipSuccess)
+    e = rr::launch_decode_select(g, reinterpret_cast<const float*>(base + w.bsum),
+                                 reinterpret_cast<const float*>(base + w.zpart), mass, row_count, col_idx, sel, w.nbp,
+                                 st);
+  if (e == hipSuccess)
+    e = rr::launch_decode_attn(g, q, k, v, row_count, col_idx, sel, w.nbp, reinterpret_cast<float*>(base + w.part),
+                               out, st);
+  return hip_status(e);
+}
+
 const char* rr_status_string(rr_status s) {
   switch (s) {
     case RR_OK: return "ok";

@@ -1,5 +1,5 @@
 // Internal launch interface between the host runtime (rr_host.cpp) and the
-// gfx950 kernels (search.hip, attn.hip, recall.hip). Not part of the public ABI.
+// gfx950 kernels (search.hip, attn.hip, recall.hip, decode.hip). Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +38,21 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
 // Selection quality: full-attention softmax mass inside the selected blocks.
 hipError_t launch_recall(const Geometry& g, const void* q, const void* k, const int32_t* row_count,
                          const int32_t* col_idx, float* recall, hipStream_t st);
+
+// Decode step (one new query per head against the cache).
+constexpr int kDecodeSplit = 16;  // list entries per split-K workgroup of the decode attention
+bool decode_grouped(const Geometry& g);  // bf16 with G <= 8: one workgroup serves a KV head's G query heads
+int decode_splits(const Geometry& g);     // split-K partials per head
+int decode_chunks(const Geometry& g);  // 256-stride chunks of the decode scores
+// per 256-stride chunk (max, exp-sum) [Hq][nchunk][2] and block sums bsum [Hq][nb] relative to the chunk max
+hipError_t launch_decode_scores(const Geometry& g, const void* q, const void* kbar, float* bsum, float* zpart,
+                                hipStream_t st);
+// block masses [Hq][nb] from the chunk partials, lists, and selection flags sel [Hq][nbp] (nbp >= nb)
+hipError_t launch_decode_select(const Geometry& g, const float* bsum, const float* zpart, float* mass,
+                                int32_t* row_count, int32_t* col_idx, uint8_t* sel, int nbp, hipStream_t st);
+hipError_t launch_decode_attn(const Geometry& g, const void* q, const void* k, const void* v,
+                              const int32_t* row_count, const int32_t* col_idx, const uint8_t* sel, int nbp,
+                              float* part, void* out, hipStream_t st);
 
 // Kernel-side limits checked by the host before any launch.
 constexpr int kMaxSelectBlocks = 8192;  // LDS sort capacity of the select kernel (nb): 12 B per key

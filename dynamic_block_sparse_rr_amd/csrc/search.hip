@@ -469,6 +469,223 @@ __global__ void __launch_bounds__(256) union_lists_kernel(const int32_t* __restr
   if (threadIdx.x < G) out_count[(size_t)(g * G + threadIdx.x) * nb + i] = (int32_t)total;
 }
 
+// Decode step: per query head, the block masses from the scores' chunk
+// partials, then the Top-tau prefix of the (mass desc, index asc) order plus
+// the last block, which holds the query itself. Written as the ascending list
+// and as flags sel[h][j] in {0, 1}.
+//
+// No sort: the cut is found by a radix search over the order key ~bits(mass)
+// (ascending key = descending mass) in 11-, 11- and 10-bit digits. The masses
+// (which sum to 1) are summed as 64-bit fixed point, m_j * 2^40, so every
+// partial sum is exact and independent of the summation order. Block j is kept
+// when the mass before it in the order is below tau * total: each pass
+// histograms the candidates' next digit (count and mass), and the cut bucket is
+// the last non-empty one whose preceding mass is still below the threshold;
+// the search stops once that bucket holds a single block. Equal masses (one key
+// value) are kept in index order while the mass before each stays below it.
+constexpr int kRadixBuckets = 2048;
+constexpr int kRadixPer = kRadixBuckets / 256;  // buckets per thread in the scans
+
+template <typename U>
+__device__ __forceinline__ U wave_scan_incl(U x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const U y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ unsigned long long to_fixed(float m) {
+  return (unsigned long long)(m * 1099511627776.0f);  // 2^40
+}
+
+__global__ void __launch_bounds__(256) decode_select_kernel(const float* __restrict__ bsum,
+                                                            const float* __restrict__ zpart, int r, int nchunk,
+                                                            float* __restrict__ mass, int nb, float tau,
+                                                            int32_t* __restrict__ row_count,
+                                                            int32_t* __restrict__ col_idx,
+                                                            uint8_t* __restrict__ sel, int nbp) {
+  extern __shared__ float mm[];  // the head's nb block masses
+  __shared__ uint32_t cnt[kRadixBuckets];
+  __shared__ unsigned long long msum[kRadixBuckets];
+  __shared__ unsigned long long wtot[4], wscan[4];
+  __shared__ uint32_t wt32[4];
+  __shared__ int slot_d[4];
+  __shared__ uint32_t slot_n[4];
+  __shared__ unsigned long long slot_b[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = blockIdx.x;
+  int32_t* out = col_idx + (size_t)h * nb;
+  uint8_t* srow = sel + (size_t)h * nbp;
+  const bool all = !(tau > 0.0f && tau < 1.0f);  // every block
+
+  for (int b = tid; b < kRadixBuckets; b += 256) {
+    cnt[b] = 0;
+    msum[b] = 0;
+  }
+  // softmax over all strides from the chunks' (max, exp-sum), every wave alike
+  const float* zp = zpart + (size_t)h * nchunk * 2;
+  float M = -INFINITY;
+  for (int c = lane; c < nchunk; c += 64) M = fmaxf(M, zp[2 * c]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float S = 0.0f;
+  for (int c = lane; c < nchunk; c += 64) S += zp[2 * c + 1] * __builtin_amdgcn_exp2f(zp[2 * c] - M);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o);
+  const float inv_s = 1.0f / S;
+  __syncthreads();  // histogram cleared
+
+  // masses, their fixed-point total and the first digit's histogram
+  unsigned long long fsum = 0;
+  for (int j = tid; j < nb; j += 256) {
+    const int ch = (j * r) >> 8;
+    float m = bsum[(size_t)h * nb + j] * __builtin_amdgcn_exp2f(zp[2 * ch] - M) * inv_s;
+    mass[(size_t)h * nb + j] = m;
+    m = m > 0.0f ? m : 0.0f;  // NaN and negative count as 0
+    mm[j] = m;
+    if (!all) {
+      const unsigned long long f = to_fixed(m);
+      fsum += f;
+      const uint32_t d = ~__float_as_uint(m) >> 21;
+      atomicAdd(&cnt[d], 1u);
+      atomicAdd(&msum[d], f);
+    }
+  }
+  if (all) {
+    for (int j = tid; j < nb; j += 256) {
+      out[j] = j;
+      srow[j] = 1;
+    }
+    if (tid == 0) row_count[h] = nb;
+    return;
+  }
+  fsum = wave_scan_incl(fsum, lane);
+  if (lane == 63) wtot[w] = fsum;
+  __syncthreads();
+  const unsigned long long TF = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  const double thr = (double)tau * (double)TF;
+  const bool none = !(thr > 0.0);  // all masses zero: keep the first block of the order only
+
+  uint32_t prefix = 0;
+  unsigned long long base = 0;
+  int fshift = 0;     // the cut is (key >> fshift) == prefix
+  uint32_t ncut = 0;  // blocks with that key prefix
+  if (!none) {
+    const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+#pragma unroll
+    for (int pss = 0; pss < 3; ++pss) {
+      const int sh = shifts[pss], wd = widths[pss];
+      if (pss > 0) {  // histogram of the candidates' next digit (cleared at the end of the last pass)
+        for (int j = tid; j < nb; j += 256) {
+          const uint32_t key = ~__float_as_uint(mm[j]);
+          if ((key >> (sh + wd)) == prefix) {
+            const uint32_t d = (key >> sh) & ((1u << wd) - 1u);
+            atomicAdd(&cnt[d], 1u);
+            atomicAdd(&msum[d], to_fixed(mm[j]));
+          }
+        }
+        __syncthreads();
+      }
+      // thread t owns buckets kRadixPer t ..: the mass before each bucket
+      uint32_t bc[kRadixPer];
+      unsigned long long bm[kRadixPer], loc = 0;
+#pragma unroll
+      for (int e = 0; e < kRadixPer; ++e) {
+        bc[e] = cnt[kRadixPer * tid + e];
+        bm[e] = msum[kRadixPer * tid + e];
+        loc += bm[e];
+      }
+      const unsigned long long inc = wave_scan_incl(loc, lane);
+      if (lane == 63) wscan[w] = inc;
+      __syncthreads();
+      unsigned long long ex = base + inc - loc;
+      for (int i = 0; i < w; ++i) ex += wscan[i];
+      int cand = -1;
+      uint32_t ccnt = 0;
+      unsigned long long cbase = 0;
+#pragma unroll
+      for (int e = 0; e < kRadixPer; ++e) {
+        if (bc[e] > 0 && (double)ex < thr) {
+          cand = kRadixPer * tid + e;
+          ccnt = bc[e];
+          cbase = ex;
+        }
+        ex += bm[e];
+      }
+      // the last qualifying bucket: per wave its highest lane, then the last wave with one
+      const unsigned long long q = __ballot(cand >= 0);
+      if (q != 0 && lane == 63 - __clzll(q)) {
+        slot_d[w] = cand;
+        slot_n[w] = ccnt;
+        slot_b[w] = cbase;
+      } else if (q == 0 && lane == 0) {
+        slot_d[w] = -1;
+      }
+#pragma unroll
+      for (int e = 0; e < kRadixPer; ++e) {  // clear for the next pass (this thread's reads are done)
+        cnt[kRadixPer * tid + e] = 0;
+        msum[kRadixPer * tid + e] = 0;
+      }
+      __syncthreads();
+      int ws = 3;
+      while (ws > 0 && slot_d[ws] < 0) --ws;
+      // slot_d[ws] >= 0: the candidates' first block has mass before it base < thr
+      prefix = (prefix << wd) | (uint32_t)slot_d[ws];
+      base = slot_b[ws];
+      ncut = slot_n[ws];
+      fshift = sh;
+      if (ncut == 1) break;
+      // the slots and wscan are rewritten only after the next pass's first
+      // barrier, which every thread reaches after its reads here
+    }
+  }
+
+  // ties (one key value, fshift == 0): the first tkeep of them in index order
+  const bool tied = !none && ncut > 1;
+  uint32_t tkeep = ncut;
+  if (tied) {
+    const unsigned long long Fs = to_fixed(__uint_as_float(~prefix));
+    if (Fs > 0) tkeep = (uint32_t)fmin((double)ncut, ceil((thr - (double)base) / (double)Fs));
+  }
+  const int seg = (nb + 255) / 256;
+  const int jlo = min(tid * seg, nb), jhi = min(jlo + seg, nb);
+  uint32_t trank = 0;
+  if (tied) {  // rank of this thread's first tie in index order
+    uint32_t ties = 0;
+    for (int j = jlo; j < jhi; ++j) ties += (~__float_as_uint(mm[j]) >> fshift) == prefix;
+    const uint32_t inc = wave_scan_incl(ties, lane);
+    __syncthreads();
+    if (lane == 63) wt32[w] = inc;
+    __syncthreads();
+    trank = inc - ties;
+    for (int i = 0; i < w; ++i) trank += wt32[i];
+  }
+  auto kept = [&](int j, uint32_t& rk) -> bool {
+    const uint32_t k = ~__float_as_uint(mm[j]) >> fshift;
+    const bool tie = tied && k == prefix;
+    const bool keep = j == nb - 1 || (none ? j == 0 : (k < prefix || (k == prefix && (!tied || rk < tkeep))));
+    rk += tie;
+    return keep;
+  };
+  uint32_t c = 0, rk = trank;
+  for (int j = jlo; j < jhi; ++j) c += kept(j, rk);
+  const uint32_t inc = wave_scan_incl(c, lane);
+  __syncthreads();
+  if (lane == 63) wt32[w] = inc;
+  __syncthreads();
+  uint32_t pos = inc - c;
+  for (int i = 0; i < w; ++i) pos += wt32[i];
+  rk = trank;
+  for (int j = jlo; j < jhi; ++j) {
+    const bool kj = kept(j, rk);
+    srow[j] = (uint8_t)kj;
+    if (kj) out[pos++] = j;
+  }
+  if (tid == 0) row_count[h] = (int32_t)(wt32[0] + wt32[1] + wt32[2] + wt32[3]);
+}
+
 template <typename T, int D>
 hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, float* mass,
                            hipStream_t st) {
@@ -541,6 +758,14 @@ hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const
   const size_t lds = 2 * (size_t)((g.nb + 31) / 32) * sizeof(uint32_t);
   union_lists_kernel<<<dim3((unsigned)(g.Hkv * g.nb)), 256, lds, st>>>(row_count, col_idx, out_count, out_idx,
                                                                       g.nb, g.G);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_decode_select(const Geometry& g, const float* bsum, const float* zpart, float* mass,
+                                int32_t* row_count, int32_t* col_idx, uint8_t* sel, int nbp, hipStream_t st) {
+  decode_select_kernel<<<dim3((unsigned)g.Hq), 256, (size_t)g.nb * sizeof(float), st>>>(
+      bsum, zpart, g.r, decode_chunks(g), mass, g.nb, g.tau, row_count, col_idx, sel, nbp);
   return hipGetLastError();
 }
 

@@ -183,6 +183,38 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
                             const void* k, const void* v, void* out, int32_t* row_count, int32_t* col_idx,
                             void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Decode step: one new query per head against the KV cache (the TL;DR names
+ * decode-stage sparsification as future work; this applies the prefill's
+ * pieces to it). p->L is the cache length, the new token's own key and value
+ * included at position L - 1; q is [Hq][d], k and v [L][Hkv][d], out [Hq][d],
+ * all in p->dtype. Per query head: scores of q against every pooled cache key
+ * (stride means as in rr_pattern_search, scale 1/sqrt(d)), one softmax over
+ * the strides, summed into key blocks; the Top-tau prefix of the (mass desc,
+ * index asc) order is kept plus the last block (the one holding the query),
+ * and q attends to every key of the kept blocks (p->tau NaN or outside
+ * (0, 1): every block). p->causal is not used. All pointers are device
+ * memory owned by the caller; the calls are asynchronous on `stream`. Errors:
+ * RR_ERR_INVALID_ARG for a NULL or unaligned (16-byte) required pointer,
+ * RR_ERR_WORKSPACE for ws_bytes below rr_decode_workspace_bytes(p),
+ * RR_ERR_UNSUPPORTED for shapes without kernels (as rr_prefill).
+ *   kbar        optional device input [ceil(L/S)][Hkv][d] in p->dtype: the
+ *               cache's pooled keys (rr_pool_keys), which a server can keep
+ *               with its cache; NULL pools them here (one pass over K).
+ *   row_count   device output int32 [Hq]; col_idx int32 [Hq][nb] (ascending).
+ *   block_mass  optional device output float [Hq][nb] (NULL to skip).
+ *   ws          rr_decode_workspace_bytes(p) bytes.
+ */
+size_t rr_decode_workspace_bytes(const rr_problem* p);
+rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar, void* out,
+                    int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* The pooled keys of rr_pattern_search's first step, on their own: kbar
+ * [ceil(L/S)][Hkv][d] in p->dtype receives, per stride of S tokens (the last
+ * possibly short), the float32 mean of its keys rounded to the dtype. */
+rr_status rr_pool_keys(const rr_problem* p, const void* k, void* kbar, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* rr_status_string(rr_status s);
 

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
                             "rr_prefill", "rr_mass_recall", "rr_share_group_lists", "rr_status_string",
                             "rr_version", "rr_pattern_search_heads", "rr_workspace_bytes_varlen",
-                            "rr_prefill_varlen"])
+                            "rr_prefill_varlen", "rr_decode_workspace_bytes", "rr_decode", "rr_pool_keys"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -154,3 +154,24 @@ def test_varlen_and_per_head_checks_on_host():
     w = rr.rr_workspace_bytes(q)
     assert lib.rr_pattern_search_heads(ctypes.byref(q), ok, ok, None, ok, ok, None, ok, w, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_pattern_search_heads(ctypes.byref(q), ok, ok, ok + 2, ok, ok, None, ok, w, 0) == rr.RR_ERR_INVALID_ARG
+
+
+def test_decode_checks_on_host():
+    lib = rr.load()
+    ok = 1 << 20
+    p = base(L=131072)
+    need = rr.rr_decode_workspace_bytes(p)
+    al = lambda x: -(-x // 256) * 256
+    ns, nb = 131072 // 16, 131072 // 128
+    # pooled keys | block sums [Hq][nb] | chunk partials [Hq][ns/256][2] | masses [Hq][nb] | flags [Hq][nb] bytes |
+    # split partials [Hq][nb/16][d+2] (16 blocks per workgroup: about 512 workgroups over nb * Hkv blocks)
+    assert need == (al(ns * 8 * 128 * 2) + al(32 * nb * 4) + al(32 * (ns // 256) * 2 * 4) + al(32 * nb * 4)
+                    + al(32 * nb) + al(32 * (nb // 16) * 130 * 4))
+    assert lib.rr_decode(ctypes.byref(p), None, ok, ok, None, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, None, ok + 2, ok, ok, None, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, ok + 8, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, None, ok, ok, ok, None, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
+    assert lib.rr_decode(ctypes.byref(base(d=96)), ok, ok, ok, None, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_UNSUPPORTED
+    assert lib.rr_pool_keys(ctypes.byref(p), ok, None, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_pool_keys(ctypes.byref(base(S=48)), ok, ok, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode_workspace_bytes(None) == 0
