@@ -36,20 +36,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload_name: str, tau: float):
+def measured_traffic(workload_name: str, tau: float, record: str = "attn_bf16", source: str = "attn.hip"):
     """HBM bytes per attention call from the committed counter record, or None.
 
-    The record (profiles/attn_bf16_<workload>_traffic.json) holds FETCH_SIZE and
+    The record (profiles/<record>_<workload>_traffic.json) holds FETCH_SIZE and
     WRITE_SIZE of the attention kernel scaled against a plain 1 GiB copy, and the
     sha256 of the kernel source they were taken on; a changed kernel reports None.
     """
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "attn_bf16_%s_traffic.json" % workload_name)
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (record, workload_name))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "csrc", "attn.hip")
+    src = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "csrc", source)
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("kernel_source_sha256"):
         return None
     if abs(float(rec.get("tau", -1)) - tau) > 1e-9:
@@ -214,7 +214,8 @@ def bench_decode(args):
         rc = torch.empty((w.Hq,), dtype=torch.int32, device="cuda")
         ci = torch.empty((w.Hq, w.nb), dtype=torch.int32, device="cuda")
         ws = torch.empty(rr.rr_decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        rr.rr_pool_keys(p, k, kbar, stream=stream)  # first launch loads the code object
         e[0].record(stream)
         rr.rr_pool_keys(p, k, kbar, stream=stream)
         e[1].record(stream)
@@ -225,8 +226,16 @@ def bench_decode(args):
         for _ in range(n):
             rr.rr_decode(p, q, k, v, out, rc, ci, None, ws, stream=stream, kbar=kbar)
         e[3].record(stream)
+        # the attention stage alone on the same lists (lists to flags, split-K attention, combine)
+        out2 = torch.empty_like(q)
+        rr.rr_decode_attend(p, q, k, v, rc, ci, out2, ws, stream=stream)
+        e[4].record(stream)
+        for _ in range(n):
+            rr.rr_decode_attend(p, q, k, v, rc, ci, out2, ws, stream=stream)
+        e[5].record(stream)
         torch.cuda.synchronize()
         us = e[2].elapsed_time(e[3]) * 1e3 / n
+        att_us = e[4].elapsed_time(e[5]) * 1e3 / n
         rcn, cin = rc.cpu().numpy(), ci.cpu().numpy()
         # algorithmic bytes: K and V of the blocks each KV head's query heads selected (their union),
         # the pooled keys once, the queries and outputs
@@ -238,9 +247,12 @@ def bench_decode(args):
                 sel.update(int(j) for j in cin[h, : rcn[h]])
             union += len(sel)
         esz = 2 if w.dtype == "bf16" else 4
-        nbytes = union * tile + p.ns * w.Hkv * w.d * esz + 2 * w.Hq * w.d * esz
-        res[t] = {"us": us, "pool_us": e[0].elapsed_time(e[1]) * 1e3, "kept": float(rcn.mean() / w.nb),
-                  "bytes": nbytes, "tbps": nbytes / (us * 1e-6) / 1e12}
+        att_bytes = union * tile + 2 * w.Hq * w.d * esz
+        nbytes = att_bytes + p.ns * w.Hkv * w.d * esz
+        res[t] = {"us": us, "att_us": att_us, "pool_us": e[0].elapsed_time(e[1]) * 1e3,
+                  "kept": float(rcn.mean() / w.nb), "union": union / (w.Hkv * w.nb),
+                  "bytes": nbytes, "tbps": nbytes / (us * 1e-6) / 1e12,
+                  "att_bytes": att_bytes, "att_tbps": att_bytes / (att_us * 1e-6) / 1e12}
     r, d_ = res[tau], res[1.0]
     line = {
         "metric": "decode step us per layer at 128K (one new token, pooled keys kept with the cache)",
@@ -249,14 +261,22 @@ def bench_decode(args):
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name + "_decode", "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "B": w.B,
                    "S": w.S, "tau": tau},
-        "blocks_kept": round(r["kept"], 4),
-        "roofline": {"bound": "hbm", "achieved": round(r["tbps"] * 1e3, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(r["tbps"] / 8.0, 4), "traffic": None,
-                     "algorithmic_bytes": r["bytes"]},
+        "blocks_kept": round(r["kept"], 4), "blocks_read_per_kv_head": round(r["union"], 4),
+        # dominant stage: the split-K attention (HIP events around rr_decode_attend, which also runs the
+        # small list-to-flag and combine kernels); bytes = K and V of the union of each KV head's
+        # selected blocks, plus the queries and outputs
+        "roofline": {"bound": "hbm", "achieved": round(r["att_tbps"] * 1e3, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(r["att_tbps"] / 8.0, 4), "traffic": None,
+                     "algorithmic_bytes": r["att_bytes"], "stage_us": round(r["att_us"], 2)},
+        "step_GBps": round(r["tbps"] * 1e3, 1), "step_algorithmic_bytes": r["bytes"],
         "dense_decode_us": round(d_["us"], 2), "dense_decode_GBps": round(d_["tbps"] * 1e3, 1),
         "speedup_vs_dense": round(d_["us"] / r["us"], 3),
         "pool_keys_us_whole_cache": round(r["pool_us"], 1),
     }
+    tr = measured_traffic(w.name, tau, record="decode_attn_bf16", source="decode.hip")
+    if tr is not None:
+        line["roofline"]["traffic"] = tr[0]
+        line["roofline"]["traffic_unit"] = "bytes per attention kernel launch (HBM, FETCH_SIZE + WRITE_SIZE)"
     print(json.dumps(line), flush=True)
 
 
@@ -283,10 +303,23 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
                          "reported as cold_* fields, events only")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="run the hbm_read probe: plain and block-walk reads of a K/V cache of the workload's "
+                         "shape, the practical read ceiling of the decode attention")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
                          "scaling HBM byte counters")
     args = ap.parse_args()
+    if args.hbm_ceiling:  # a child process of its own, before this one touches the GPU
+        import subprocess
+
+        from synthetic.gen import workload as wl
+
+        w = wl(args.workload)
+        probe = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "hbm_read")
+        if not os.path.exists(probe):
+            raise SystemExit("hbm_read is not built: run python -m dynamic_block_sparse_rr_amd.build")
+        sys.exit(subprocess.run([probe, str(w.L), str(w.Hkv)]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the operator is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
@@ -297,6 +330,12 @@ def main():
     import dynamic_block_sparse_rr_amd as rr
     from synthetic.gen import make_inputs, workload
 
+    if args.calib_copy:  # a plain 1 GiB device copy first: the reference for HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.varlen:
         return bench_varlen(args)
     if args.decode:
@@ -308,12 +347,6 @@ def main():
     q, k, v = make_inputs(w)
     log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    if args.calib_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     p = rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, tau, w.causal, w.dtype)
     pre = rr.Prefill(p)
     stream = torch.cuda.current_stream()

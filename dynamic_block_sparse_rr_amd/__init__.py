@@ -89,6 +89,8 @@ def load():
         lib.rr_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.rr_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.rr_decode.restype = ctypes.c_int
+        lib.rr_decode_attend.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.rr_decode_attend.restype = ctypes.c_int
         lib.rr_pool_keys.argtypes = [PP, P, P, P]
         lib.rr_pool_keys.restype = ctypes.c_int
         lib.rr_status_string.argtypes = [ctypes.c_int]
@@ -209,6 +211,12 @@ def rr_decode(p, q, k, v, out, row_count, col_idx, block_mass, ws, ws_bytes=None
     _check("rr_decode", load().rr_decode(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), _ptr(out), _ptr(row_count), _ptr(col_idx),
         _ptr(block_mass), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+
+
+def rr_decode_attend(p, q, k, v, row_count, col_idx, out, ws, ws_bytes=None, stream=None):
+    _check("rr_decode_attend", load().rr_decode_attend(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_count), _ptr(col_idx), _ptr(out), _ptr(ws),
+        _nbytes(ws, ws_bytes), _stream(stream)))
 
 
 def rr_pool_keys(p, k, kbar, stream=None):

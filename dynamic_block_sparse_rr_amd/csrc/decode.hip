@@ -128,16 +128,16 @@ __global__ void __launch_bounds__(kDecodeChunk) decode_scores_kernel(const T* __
 
 constexpr int kDecodeThreads = 256;
 
-// Split-K attention of one head's query over list entries [sp*CB, sp*CB+CB).
+// Split-K attention of one head's query (shapes without the group kernel) over
+// the selected blocks among [sp*kDecodeSplit, sp*kDecodeSplit + kDecodeSplit).
 // Per block: thread pairs (2i, 2i+1) score key i over the two halves of d;
 // then thread t accumulates channels 8*(t%CG)..+7 of P V over keys
 // (t/CG)*KG..+KG-1 with 16-byte loads, and the key groups are summed in LDS
 // in a fixed order into the workgroup's O.
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(kDecodeThreads) decode_attn_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ row_count,
-    const int32_t* __restrict__ col_idx, float* __restrict__ part, int Hq, int Hkv, int nb, int L, float cscale,
-    int nsplit) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const uint8_t* __restrict__ sel, int nbp,
+    float* __restrict__ part, int Hq, int Hkv, int nb, int L, float cscale, int nsplit) {
   constexpr int CG = D / 8;                   // channel groups of 8 (16 bytes of bf16)
   constexpr int NKG = kDecodeThreads / CG;    // key groups
   constexpr int KG = BLK / NKG;               // keys per group
@@ -150,14 +150,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_attn_kernel(
   const int t = threadIdx.x;
   for (int e = t; e < D; e += kDecodeThreads) qs[e] = to_float(q[(size_t)h * D + e]);
   __syncthreads();
-  const int cnt = min(max(row_count[h], 0), nb);
-  const int c0 = sp * kDecodeSplit, c1 = min(c0 + kDecodeSplit, cnt);
+  const int j0 = sp * kDecodeSplit, j1 = min(j0 + kDecodeSplit, nb);
   const int cg = t % CG, kgi = t / CG;
   float m = -INFINITY, l = 0.0f;
   float o[8];  // channels 8*cg.. of the key group's partial, merged each block into O (threads t < D own O[t])
   float O = 0.0f;
-  for (int c = c0; c < c1; ++c) {
-    const int j = min(max(col_idx[(size_t)h * nb + c], 0), nb - 1);
+  for (int j = j0; j < j1; ++j) {
+    if (!sel[(size_t)h * nbp + j]) continue;  // the same for the whole workgroup
     const int nkeys = min(BLK, L - j * BLK);
     // scores: thread 2i + hf scores half hf of key i (keys beyond BLK / nkeys idle)
     const int key = t >> 1, hf = t & 1;
@@ -348,19 +347,19 @@ __global__ void __launch_bounds__(256, 2) decode_group_attn_kernel(
     lst[i] = 0.0f;
   }
 
-  // K rows for the MFMA B operand and V chunks for the PV phase of block j
+  // K rows for the MFMA B operand and V chunks for the PV phase of block j;
+  // the loads are unconditional (clamped rows) so that the next block's stay
+  // in flight while the current one is computed
   auto load_k = [&](int j, u32x4 (&kr)[KT * NS]) {
     const int nkeys = min(BLK, L - j * BLK);
     const __bf16* kb = k + (size_t)j * BLK * row + (size_t)g * D;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int key = w * (BLK / 4) + kt * 16 + (lane & 15);
+      const int kc = min(key, nkeys - 1);  // rows past the cache end: scores masked later
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < nkeys) x = *reinterpret_cast<const u32x4*>(kb + (size_t)key * row + 32 * s + 8 * (lane >> 4));
-        kr[kt * NS + s] = x;
-      }
+      for (int s = 0; s < NS; ++s)
+        kr[kt * NS + s] = *reinterpret_cast<const u32x4*>(kb + (size_t)kc * row + 32 * s + 8 * (lane >> 4));
     }
   };
   auto load_v = [&](int j, vword (&vr)[KG]) {
@@ -369,9 +368,8 @@ __global__ void __launch_bounds__(256, 2) decode_group_attn_kernel(
 #pragma unroll
     for (int kk = 0; kk < KG; ++kk) {
       const int y = kgi * KG + kk;
-      vword x = {};
-      if (y < nkeys) x = *reinterpret_cast<const vword*>(vb + (size_t)y * row + CPT * cg);
-      vr[kk] = x;
+      // keys past the cache end read the last row and get probability 0
+      vr[kk] = *reinterpret_cast<const vword*>(vb + (size_t)min(y, nkeys - 1) * row + CPT * cg);
     }
   };
 
@@ -461,15 +459,17 @@ __global__ void __launch_bounds__(256, 2) decode_group_attn_kernel(
     load_v(act_j[0], va);
   }
   for (int a = 0; a < nact; a += 2) {
-    if (a + 1 < nact) {
-      load_k(act_j[a + 1], kb2);
-      load_v(act_j[a + 1], vb2);
+    {  // the next block, or this one again at the end (cache hits, unused)
+      const int jn = act_j[a + 1 < nact ? a + 1 : a];
+      load_k(jn, kb2);
+      load_v(jn, vb2);
     }
     process(act_j[a], act_m[a], ka, va);
     if (a + 1 >= nact) break;
-    if (a + 2 < nact) {
-      load_k(act_j[a + 2], ka);
-      load_v(act_j[a + 2], va);
+    {
+      const int jn = act_j[a + 2 < nact ? a + 2 : a + 1];
+      load_k(jn, ka);
+      load_v(jn, va);
     }
     process(act_j[a + 1], act_m[a + 1], kb2, vb2);
   }
@@ -660,8 +660,29 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(const float* __rest
   }
 }
 
+// Selection flags sel[h][j] from block lists (entries outside [0, nb) and a
+// count outside [0, nb] are clamped away): one workgroup per head.
+__global__ void __launch_bounds__(256) lists_to_flags_kernel(const int32_t* __restrict__ row_count,
+                                                             const int32_t* __restrict__ col_idx, int nb,
+                                                             uint8_t* __restrict__ sel, int nbp) {
+  const int h = blockIdx.x;
+  uint8_t* srow = sel + (size_t)h * nbp;
+  for (int j = threadIdx.x; j < nb; j += 256) srow[j] = 0;
+  __syncthreads();
+  const int cnt = min(max(row_count[h], 0), nb);
+  for (int c = threadIdx.x; c < cnt; c += 256) {
+    const int j = col_idx[(size_t)h * nb + c];
+    if (j >= 0 && j < nb) srow[j] = 1;
+  }
+}
+
 }  // namespace
 
+hipError_t launch_lists_to_flags(const Geometry& g, const int32_t* row_count, const int32_t* col_idx, uint8_t* sel,
+                                 int nbp, hipStream_t st) {
+  lists_to_flags_kernel<<<dim3((unsigned)g.Hq), 256, 0, st>>>(row_count, col_idx, g.nb, sel, nbp);
+  return hipGetLastError();
+}
 
 int decode_chunks(const Geometry& g) { return (g.ns + kDecodeChunk - 1) / kDecodeChunk; }
 
@@ -740,8 +761,8 @@ hipError_t launch_decode_attn(const Geometry& g, const void* q, const void* k, c
 #define RR_DA(TY, DV, BV)                                                                                     \
   if (!launched && g.d == DV && g.B == BV) {                                                                  \
     decode_attn_kernel<TY, DV, BV><<<grid, kDecodeThreads, 0, st>>>(                                          \
-        static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v), row_count, col_idx, \
-        part, g.Hq, g.Hkv, g.nb, g.L, cscale, nsplit);                                                        \
+        static_cast<const TY*>(q), static_cast<const TY*>(k), static_cast<const TY*>(v), sel, nbp, part,     \
+        g.Hq, g.Hkv, g.nb, g.L, cscale, nsplit);                                                              \
     launched = true;                                                                                          \
   }
     if (g.bf16) {

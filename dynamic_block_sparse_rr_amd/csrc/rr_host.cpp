@@ -348,6 +348,27 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
   return hip_status(e);
 }
 
+rr_status rr_decode_attend(const rr_problem* p, const void* q, const void* k, const void* v, const int32_t* row_count,
+                           const int32_t* col_idx, void* out, void* ws, size_t ws_bytes, void* stream) {
+  rr::Geometry g;
+  rr_status s = make_geometry(p, &g);
+  if (s != RR_OK) return s;
+  if (!q || !k || !v || !out || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(row_count) ||
+      !aligned16(col_idx))
+    return RR_ERR_INVALID_ARG;
+  const DecodeWorkspace w = decode_layout(g);
+  if (!ws || !aligned16(ws) || ws_bytes < w.total) return RR_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* sel = base + w.sel;
+  hipError_t e = rr::launch_lists_to_flags(g, row_count, col_idx, sel, w.nbp, st);
+  if (e == hipSuccess)
+    e = rr::launch_decode_attn(g, q, k, v, row_count, col_idx, sel, w.nbp, reinterpret_cast<float*>(base + w.part),
+                               out, st);
+  return hip_status(e);
+}
+
 const char* rr_status_string(rr_status s) {
   switch (s) {
     case RR_OK: return "ok";

@@ -50,6 +50,8 @@ hipError_t launch_decode_scores(const Geometry& g, const void* q, const void* kb
 // block masses [Hq][nb] from the chunk partials, lists, and selection flags sel [Hq][nbp] (nbp >= nb)
 hipError_t launch_decode_select(const Geometry& g, const float* bsum, const float* zpart, float* mass,
                                 int32_t* row_count, int32_t* col_idx, uint8_t* sel, int nbp, hipStream_t st);
+hipError_t launch_lists_to_flags(const Geometry& g, const int32_t* row_count, const int32_t* col_idx, uint8_t* sel,
+                                 int nbp, hipStream_t st);
 hipError_t launch_decode_attn(const Geometry& g, const void* q, const void* k, const void* v,
                               const int32_t* row_count, const int32_t* col_idx, const uint8_t* sel, int nbp,
                               float* part, void* out, hipStream_t st);

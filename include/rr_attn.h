@@ -210,6 +210,16 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
                     int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* The attention stage of rr_decode on its own: q attends to every key of the
+ * blocks in each head's list (row_count [Hq], col_idx [Hq][nb] int32 device
+ * inputs; entries outside [0, nb) and repeats are ignored, the order does
+ * not matter),
+ * with the same kernels and results as rr_decode for the same lists. For
+ * lists kept over several steps or chosen by the caller. ws as for rr_decode;
+ * errors as rr_decode. */
+rr_status rr_decode_attend(const rr_problem* p, const void* q, const void* k, const void* v, const int32_t* row_count,
+                           const int32_t* col_idx, void* out, void* ws, size_t ws_bytes, void* stream);
+
 /* The pooled keys of rr_pattern_search's first step, on their own: kbar
  * [ceil(L/S)][Hkv][d] in p->dtype receives, per stride of S tokens (the last
  * possibly short), the float32 mean of its keys rounded to the dtype. */

@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
                             "rr_prefill", "rr_mass_recall", "rr_share_group_lists", "rr_status_string",
                             "rr_version", "rr_pattern_search_heads", "rr_workspace_bytes_varlen",
-                            "rr_prefill_varlen", "rr_decode_workspace_bytes", "rr_decode", "rr_pool_keys"])
+                            "rr_prefill_varlen", "rr_decode_workspace_bytes", "rr_decode", "rr_decode_attend", "rr_pool_keys"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -172,6 +172,9 @@ def test_decode_checks_on_host():
     assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, ok + 8, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, None, ok, ok, ok, None, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
     assert lib.rr_decode(ctypes.byref(base(d=96)), ok, ok, ok, None, ok, ok, ok, None, ok, need, 0) == rr.RR_ERR_UNSUPPORTED
+    assert lib.rr_decode_attend(ctypes.byref(p), ok, ok, ok, None, ok, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode_attend(ctypes.byref(p), ok, ok, ok, ok, ok + 4, ok, ok, need, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode_attend(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, need - 1, 0) == rr.RR_ERR_WORKSPACE
     assert lib.rr_pool_keys(ctypes.byref(p), ok, None, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_pool_keys(ctypes.byref(base(S=48)), ok, ok, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_decode_workspace_bytes(None) == 0

@@ -127,6 +127,51 @@ def test_decode_equal_masses_keep_lowest_indices():
         assert rc.min() > 1
 
 
+def test_decode_attend_on_given_lists():
+    # rr_decode_attend on rr_decode's own lists reproduces its output bitwise;
+    # on caller lists (unordered, with entries outside [0, nb) and repeats) it
+    # attends to exactly the listed blocks
+    for (L, Hq, Hkv, d, B, dt) in [(40000, 16, 4, 128, 128, "bf16"), (3000, 6, 2, 64, 64, "bf16"),
+                                   (2000, 4, 2, 64, 64, "fp32")]:
+        w = Workload("att", L, Hq, Hkv, d, dt, B, 16 if d == 128 else 8, (0.9,), 17, "llm", 8)
+        q, k, v = make_inputs(w)
+        p = rr.problem(L, Hq, Hkv, d, w.S, B, 0.9, True, dt)
+        nb = p.nb
+        qd, kd, vd = q[L - 1].contiguous().cuda(), k.cuda(), v.cuda()
+        ws = torch.empty(rr.rr_decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        out1, out2 = torch.empty_like(qd), torch.empty_like(qd)
+        rc = torch.empty((Hq,), dtype=torch.int32, device="cuda")
+        ci = torch.full((Hq, nb), -1, dtype=torch.int32, device="cuda")
+        rr.rr_decode(p, qd, kd, vd, out1, rc, ci, None, ws)
+        rr.rr_decode_attend(p, qd, kd, vd, rc, ci, out2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out1, out2)
+        rng = np.random.default_rng(L)
+        lists, counts = np.full((Hq, nb), -1, np.int32), np.zeros(Hq, np.int32)
+        for h in range(Hq):
+            pick = rng.permutation(nb)[: max(1, nb // 3)]
+            extra = [nb + 5, -3, int(pick[0])] if h % 2 else []  # out of range, and a repeat
+            row = np.concatenate([pick, extra]).astype(np.int32)
+            lists[h, : len(row)], counts[h] = row, len(row)
+        out3 = torch.empty_like(qd)
+        rr.rr_decode_attend(p, qd, kd, vd, torch.from_numpy(counts).cuda(), torch.from_numpy(lists).cuda(), out3, ws)
+        torch.cuda.synchronize()
+        got = out3.float().cpu().numpy()
+        kf, vf, qf = k.float().numpy(), v.float().numpy(), q[L - 1].float().numpy()
+        G = Hq // Hkv
+        err = []
+        for h in range(Hq):
+            blocks = [j for j in lists[h, : counts[h]] if 0 <= j < nb]
+            keys = np.nonzero(np.repeat(np.isin(np.arange(nb), blocks), B)[:L])[0]
+            a = kf[keys, h // G, :].astype(np.float64) @ qf[h].astype(np.float64) / math.sqrt(d)
+            wgt = np.exp(a - a.max())
+            err.append(np.abs(got[h] - wgt @ vf[keys, h // G, :].astype(np.float64) / wgt.sum()))
+        e = np.concatenate(err)
+        tmax, tmean = (2e-2, 2e-3) if dt == "bf16" else (1e-4, 1e-5)
+        say(f"  decode_attend L={L} d={d} B={B} {dt}: caller lists max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+        assert e.max() <= tmax and e.mean() <= tmean
+
+
 def test_decode_tau_one_is_dense_sdpa():
     w = Workload("dense", 20000, 8, 2, 128, "bf16", 128, 16, (1.0,), 9, "llm", 8)
     q, k, v = make_inputs(w)
