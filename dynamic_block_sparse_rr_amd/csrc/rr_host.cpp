@@ -82,7 +82,7 @@ rr_status run_search(const rr::Geometry& g, const void* q, const void* k, int32_
   uint8_t* base = static_cast<uint8_t*>(ws);
   void* kbar = base + w.kbar;
   float* mass = block_mass ? block_mass : reinterpret_cast<float*>(base + w.mass);
-  hipError_t e = rr::launch_pool_keys(g, k, kbar, st);
+  hipError_t e = rr::launch_pool_keys(g, k, kbar, true, st);
   if (e == hipSuccess) e = rr::launch_search(g, q, kbar, mass, st);
   if (e == hipSuccess) e = rr::launch_select(g, mass, block_mass != nullptr, row_count, col_idx, tau_heads, st);
   return hip_status(e);
@@ -309,7 +309,7 @@ rr_status rr_pool_keys(const rr_problem* p, const void* k, void* kbar, void* str
   rr_status s = make_geometry(p, &g);
   if (s != RR_OK) return s;
   if (!k || !kbar || !aligned16(k) || !aligned16(kbar)) return RR_ERR_INVALID_ARG;
-  return hip_status(rr::launch_pool_keys(g, k, kbar, static_cast<hipStream_t>(stream)));
+  return hip_status(rr::launch_pool_keys(g, k, kbar, false, static_cast<hipStream_t>(stream)));
 }
 
 rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar, void* out,
@@ -331,7 +331,7 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (!kbar) {  // pool the cache's keys here
-    e = rr::launch_pool_keys(g, k, base + w.kbar, st);
+    e = rr::launch_pool_keys(g, k, base + w.kbar, false, st);
     kbar = base + w.kbar;
   }
   if (e == hipSuccess)

@@ -18,7 +18,9 @@ struct Geometry {
 };
 
 // Stage 1 launches.
-hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStream_t st);
+// chunk_major: kbar as [Hkv][d*esz/16][ns] 16-byte chunks (the search's layout), else [ns][Hkv][d]
+hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, bool chunk_major, hipStream_t st);
+// kbar in the chunk-major layout
 hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, float* mass,
                          hipStream_t st);
 // tau_heads: optional device thresholds [Hq] in place of g.tau.

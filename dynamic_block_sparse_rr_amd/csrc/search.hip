@@ -52,10 +52,15 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
 
 // ------------------------------------------------------------------ pooling
 
-template <typename T>
+// Pooled keys, one thread per 16-byte chunk of a pooled row (row_chunks =
+// Hkv * d * sizeof(T) / 16 per stride; reads of K coalesced). Layout of kbar:
+// row-major [ns][Hkv][d] (CM false: the public pooled-key format), or
+// chunk-major [Hkv][d*sizeof(T)/16][ns] of 16-byte chunks (CM true: the
+// search's own copy, in which the 32 strides of one MFMA operand load are
+// contiguous).
+template <typename T, bool CM>
 __global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k, T* __restrict__ kbar,
                                                         int ns, int row_chunks, int S, int L) {
-  // one thread per 16-byte chunk of a pooled row; row_chunks = Hkv * d * sizeof(T) / 16
   const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
   if (n >= (long long)ns * row_chunks) return;
   const int t = (int)(n / row_chunks);
@@ -89,7 +94,7 @@ __global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < 4; ++e) res[e] = __float_as_uint(acc[e] / fcnt);
   }
-  reinterpret_cast<u32x4*>(kbar)[n] = res;
+  reinterpret_cast<u32x4*>(kbar)[CM ? (size_t)c * ns + t : (size_t)n] = res;
 }
 
 // ------------------------------------------------------------------ scoring
@@ -166,7 +171,7 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
       const int h = h0 + hl;
       const int s = i * R + a;
       const int pos = s * S + (h % S);  // head round-robin offset
-      const chunk_t* src = reinterpret_cast<const chunk_t*>(q + ((size_t)pos * Hq + h) * D);
+      const chunk_t* src = reinterpret_cast<const chunk_t*>(q + ((size_t)pos * Hq + h) * D);  // row-major query
 #pragma unroll
       for (int c = 0; c < NCH; ++c) qf[ct][c] = src[2 * c + half];
       lim[ct] = causal ? s : ns - 1;
@@ -177,14 +182,18 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     }
   }
 
+  // pooled keys in the chunk-major layout: chunk cc of stride t of KV head g
+  // at (g * 2 * NCH + cc) * ns + t, so one operand load (32 strides, one chunk
+  // per lane half) reads two contiguous 512-byte runs
+  const chunk_t* kcm = reinterpret_cast<const chunk_t*>(kbar) + (size_t)g * 2 * NCH * ns;
+
   // ---- pass 1: running max / sum of exp2(scaled score) per sampled query
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
   for (int tile = wave; tile < ntile; tile += 4) {
     const int trow = min(tile * 32 + n32, ns - 1);
-    const chunk_t* src = reinterpret_cast<const chunk_t*>(kbar + ((size_t)trow * Hkv + g) * D);
     chunk_t kf[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[c] = src[2 * c + half];
+    for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       if (ct >= NCT) break;
@@ -236,10 +245,9 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
   const float invR = 1.0f / (float)R;  // exact
   for (int tile = wave; tile < ntile; tile += 4) {
     const int trow = min(tile * 32 + n32, ns - 1);
-    const chunk_t* src = reinterpret_cast<const chunk_t*>(kbar + ((size_t)trow * Hkv + g) * D);
     chunk_t kf[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[c] = src[2 * c + half];
+    for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       if (ct >= NCT) break;
@@ -717,17 +725,22 @@ hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, f
 
 }  // namespace
 
-hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, hipStream_t st) {
+hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, bool chunk_major, hipStream_t st) {
   const int esz = g.bf16 ? 2 : 4;
   const int row_chunks = g.Hkv * g.d * esz / 16;
   const long long n = (long long)g.ns * row_chunks;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (g.bf16)
-    pool_keys_kernel<__bf16><<<grid, 256, 0, st>>>(static_cast<const __bf16*>(k),
-                                                   static_cast<__bf16*>(kbar), g.ns, row_chunks, g.S, g.L);
-  else
-    pool_keys_kernel<float><<<grid, 256, 0, st>>>(static_cast<const float*>(k),
-                                                  static_cast<float*>(kbar), g.ns, row_chunks, g.S, g.L);
+#define RR_POOL(TY, CMV)                                                                                   \
+  pool_keys_kernel<TY, CMV><<<grid, 256, 0, st>>>(static_cast<const TY*>(k), static_cast<TY*>(kbar), g.ns, \
+                                                  row_chunks, g.S, g.L)
+  if (g.bf16) {
+    if (chunk_major) RR_POOL(__bf16, true);
+    else RR_POOL(__bf16, false);
+  } else {
+    if (chunk_major) RR_POOL(float, true);
+    else RR_POOL(float, false);
+  }
+#undef RR_POOL
   return hipGetLastError();
 }
 
