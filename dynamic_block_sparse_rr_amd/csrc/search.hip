@@ -187,6 +187,10 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
   // per lane half) reads two contiguous 512-byte runs
   const chunk_t* kcm = reinterpret_cast<const chunk_t*>(kbar) + (size_t)g * 2 * NCH * ns;
 
+  // a tile all of whose strides every sampled query sees needs no mask (the
+  // padding columns past NQ then hold values that are never written)
+  const int lim_all = causal ? i * R : ns - 1;
+
   // ---- pass 1: running max / sum of exp2(scaled score) per sampled query
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
   for (int tile = wave; tile < ntile; tile += 4) {
@@ -194,6 +198,7 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     chunk_t kf[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
+    const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       if (ct >= NCT) break;
@@ -201,11 +206,19 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
 #pragma unroll
       for (int c = 0; c < NCH; ++c) acc = Mfma<T>::acc(kf[c], qf[ct][c], acc);
       float tmax = -INFINITY;
+      if (whole) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = tile * 32 + out_row(v, half);
-        acc[v] = (t <= lim[ct]) ? acc[v] * cscale : -INFINITY;
-        tmax = fmaxf(tmax, acc[v]);
+        for (int v = 0; v < 16; ++v) {
+          acc[v] *= cscale;
+          tmax = fmaxf(tmax, acc[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = tile * 32 + out_row(v, half);
+          acc[v] = (t <= lim[ct]) ? acc[v] * cscale : -INFINITY;
+          tmax = fmaxf(tmax, acc[v]);
+        }
       }
       if (tmax > -INFINITY) {
         const float mnew = fmaxf(mrun[ct], tmax);
@@ -248,18 +261,25 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     chunk_t kf[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
+    const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       if (ct >= NCT) break;
       f32x16 acc = {};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) acc = Mfma<T>::acc(kf[c], qf[ct][c], acc);
+      // unnormalised probabilities (the query's 1/sum is applied to the in-lane block sums)
       float p[16];
+      if (whole) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = tile * 32 + out_row(v, half);
-        const float e = exp2_approx(acc[v] * cscale - mu[ct]) * invl[ct];
-        p[v] = (t <= lim[ct]) ? e : 0.0f;
+        for (int v = 0; v < 16; ++v) p[v] = exp2_approx(acc[v] * cscale - mu[ct]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = tile * 32 + out_row(v, half);
+          const float e = exp2_approx(acc[v] * cscale - mu[ct]);
+          p[v] = (t <= lim[ct]) ? e : 0.0f;
+        }
       }
       // in-lane sums over the strides of one key block, then across lane halves
       constexpr int NW = (R == 2) ? 8 : (R == 4 || R == 8) ? 4 : (R == 16) ? 2 : 1;
@@ -281,6 +301,8 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
           w[0] = (w4[0] + w4[1]) + (w4[2] + w4[3]);
         }
       }
+#pragma unroll
+      for (int k = 0; k < NW; ++k) w[k] *= invl[ct];
       if constexpr (R >= 8) {
 #pragma unroll
         for (int k = 0; k < NW; ++k) w[k] += __shfl_xor(w[k], 32);

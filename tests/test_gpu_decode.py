@@ -105,10 +105,12 @@ def test_decode_ragged_cache_and_small_shapes():
 
 
 def test_decode_group_shapes():
-    # query heads per KV head 3, 5, 8 and 1 with 64 blocks per workgroup (the most), over every d x B
+    # query heads per KV head 3, 5, 8 and 1 with 64 blocks per workgroup (the most), over every d x B,
+    # and 10 (past the group kernels)
     for (L, Hq, Hkv, d, S, B, kind) in [(9000, 24, 3, 128, 16, 64, "llm"), (12345, 15, 3, 64, 8, 128, "gauss"),
                                          (3000, 6, 2, 128, 16, 128, "llm"), (32768, 64, 64, 64, 16, 64, "gauss"),
-                                         (64, 8, 1, 128, 16, 128, "llm")]:
+                                         (64, 8, 1, 128, 16, 128, "llm"),
+                                         (5000, 20, 2, 128, 16, 128, "llm")]:  # G = 10: the per-head kernels in bf16
         w = Workload("dec", L, Hq, Hkv, d, "bf16", B, S, (0.9,), 11, kind, 8)
         q, k, v = make_inputs(w)
         say(f"decode group case L={L} Hq={Hq} Hkv={Hkv} d={d} B={B}")
