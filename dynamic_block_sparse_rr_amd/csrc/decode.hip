@@ -5,19 +5,21 @@
 // query itself in place of the round-robin samples:
 //   decode_scores   workgroup (KV head, chunk of 256 strides): the G query
 //                   heads' scores against the pooled cache keys (stride means,
-//                   as in prefill) on MFMA, with each chunk's max and exp-sum;
+//                   as in prefill) on MFMA, with each chunk's max and exp-sum
+//                   and its key blocks' exp-sums;
 //   (select)        search.hip's decode_select_kernel, one workgroup per head:
 //                   the chunks merged into one softmax over the strides, summed
 //                   into block masses, then the Top-tau prefix of the (mass
 //                   desc, index asc) order plus the last block;
 //   decode_attn     split-K attention over the selected blocks: workgroup
-//                   (KV head, range of blocks) reads each block that any of
-//                   its G query heads selected once, with an online softmax
-//                   per head, and leaves (max, sum, O) partials;
+//                   (KV head, equal share of the blocks any of its G query
+//                   heads selected) reads each block once for all G heads, with
+//                   an online softmax per head, and leaves (max, sum, O)
+//                   partials;
 //   decode_combine  one workgroup per head merges its partials in split order.
-// The step is memory-bound: the selected blocks' K and V are read once per
-// query head (the G heads of a KV head read overlapping blocks, which L2
-// shares), a few hundred MiB at 128K.
+// bf16 with G <= 8 takes the group kernels; other shapes take per-head ones
+// with the same results. The step is memory-bound: the K and V of the union of
+// each KV head's selections, read once, a few hundred MB at 128K.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -273,7 +275,6 @@ __global__ void __launch_bounds__(256, 2) decode_group_attn_kernel(
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
-  const int Hq = Hkv * G;
   const size_t row = (size_t)Hkv * D;  // elements between consecutive keys
 
   // active blocks: those any of the G heads selected, ranked in block order;
@@ -332,7 +333,6 @@ __global__ void __launch_bounds__(256, 2) decode_group_attn_kernel(
   }
   __syncthreads();
   const int nact = nact_s;
-  (void)Hq;
 
   const int cg = t % CG, kgi = t / CG;
   float o[G][CPT];
@@ -561,9 +561,7 @@ __global__ void __launch_bounds__(256) decode_group_scores_kernel(const __bf16* 
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], __builtin_bit_cast(bf16x8, kr[kt][s]), acc, 0, 0, 0);
     const int t = ch * 256 + w * 64 + kt * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * (lane >> 4) + i;
-      (void)h;
+    for (int i = 0; i < 4; ++i) {  // row 4 (lane / 16) + i: a head of the group (or padding)
       z[kt][i] = t < ns ? acc[i] * cscale : -INFINITY;
       mx[i] = fmaxf(mx[i], z[kt][i]);
     }
