@@ -98,7 +98,8 @@ def test_decode_workload_last_token(name, tau):
 
 def test_decode_ragged_cache_and_small_shapes():
     for (L, Hq, Hkv, d, S, B, dt, kind) in [(100001, 8, 2, 128, 16, 128, "bf16", "llm"), (5000, 4, 4, 64, 8, 64, "bf16", "gauss"),
-                                             (777, 2, 1, 64, 8, 64, "fp32", "tiny"), (130, 4, 2, 128, 16, 128, "bf16", "gauss")]:
+                                             (777, 2, 1, 64, 8, 64, "fp32", "tiny"), (130, 4, 2, 128, 16, 128, "bf16", "gauss"),
+                                             (1, 4, 2, 128, 16, 128, "bf16", "gauss"), (17, 8, 2, 128, 16, 128, "bf16", "gauss")]:
         w = Workload("dec", L, Hq, Hkv, d, dt, B, S, (0.9,), 7, kind, 8)
         q, k, v = make_inputs(w)
         check(q[L - 1], k, v, S, B, 0.9, dt, f"L{L}_d{d}_B{B}_{dt}")

@@ -34,6 +34,9 @@ RAGGED = [
     g("fp32_tail52", 500, 2, 1, 64, 8, 64, "fp32", kind="tiny"),
     g("fp32_noncausal_tail52", 500, 2, 1, 64, 8, 64, "fp32", causal=False),
     g("single_short_block", 50, 4, 2, 64, 8, 64, "bf16"),                      # nb = 1
+    g("one_token", 1, 4, 2, 128, 16, 128, "bf16"),                              # L = 1: one key, one stride
+    g("two_tokens_noncausal", 2, 4, 2, 128, 16, 128, "bf16", causal=False),
+    g("seventeen_tokens", 17, 8, 2, 128, 16, 128, "bf16"),                      # one short block, a short stride
 ]
 
 
