@@ -1,7 +1,7 @@
 // Stage 2 of RRAttention on gfx950: block-sparse flash attention over the
-// compacted per-row block lists ("computing only half of the attention
-// blocks", abstract of "RRAttention: Dynamic Block Sparse Attention via
-// Per-Head Round-Robin Shifts for Long-Context Inference").
+// compacted per-row block lists (the abstract of "RRAttention: Dynamic Block
+// Sparse Attention via Per-Head Round-Robin Shifts for Long-Context
+// Inference" reports about half of the blocks computed).
 //
 // bfloat16 path (the hot kernel)
 //   transpose_v  V [L][Hkv][d] -> Vt [Hkv][nb][d][B]: each key block becomes a

@@ -3,10 +3,11 @@
 // Top-tau block selection with the last query block kept whole.
 //
 // Method: "RRAttention: Dynamic Block Sparse Attention via Per-Head
-// Round-Robin Shifts for Long-Context Inference" -- abstract (head
-// round-robin sampling, stride-level aggregation, O(L^2/S^2), adaptive
-// Top-tau), TL;DR (Top-tau block selection, static protection of the last
-// query block), Figure 2 caption (stride S, block B, three stages).
+// Round-Robin Shifts for Long-Context Inference" -- abstract (sampling
+// positions rotated over the heads, keys aggregated per stride, the
+// O(L^2/S^2) search cost, the adaptive Top-tau cut), TL;DR (Top-tau block
+// selection; the last query block always kept whole), Figure 2 caption
+// (stride S, block B, three stages).
 //
 // Kernels
 //   pool_keys   K [L][Hkv][d] -> Kbar [ceil(L/S)][Hkv][d]: float32 sum of the

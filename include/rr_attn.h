@@ -80,9 +80,9 @@ typedef struct {
 size_t rr_workspace_bytes(const rr_problem* p);
 
 /*
- * Stage 1, the round-robin pattern search (abstract: "head round-robin
- * sampling", "stride-level aggregation", "adaptive Top-tau selection"; TL;DR:
- * "static protection of the last query block").
+ * Stage 1, the round-robin pattern search (abstract: sampling positions
+ * rotated over the heads, keys aggregated per stride, the adaptive Top-tau
+ * cut; TL;DR: the last query block is always kept whole).
  *   q, k        device inputs, [L][Hq][d] and [L][Hkv][d] in p->dtype.
  *   row_count   device output int32 [Hq][nb].
  *   col_idx     device output int32 [Hq][nb][nb] (ascending per row).
@@ -100,8 +100,8 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Stage 2, block-sparse attention over given block lists (abstract: "computing
- * only half of the attention blocks"). The lists may come from
+ * Stage 2, block-sparse attention over given block lists (abstract: only the
+ * selected blocks, about half of them, are computed). The lists may come from
  * rr_pattern_search or any other source; each row must be non-empty,
  * ascending, < nb, and (causal) <= its query block index: rows breaking this
  * give undefined output (the library does not read lists back to the host).

@@ -5,7 +5,7 @@ stripe logit boosts; for the video recipe beta scales the cross-frame patch
 band. Each is chosen by bisection so that the oracle's Top-tau search on the
 reference layer (32K tokens for the 8B shape, 64K for the video shape) at
 tau = 0.9 keeps half of the causal blocks, the regime the RRAttention pages
-report ("roughly half of the blocks", abstract and TL;DR). The result is
+report (about half of the blocks, abstract and TL;DR). The result is
 written to generator_calibration.json; the constants in synthetic/gen.py are
 the rounded values from that record.
 
