@@ -555,6 +555,15 @@ __global__ void __launch_bounds__(256) decode_select_kernel(const float* __restr
     cnt[b] = 0;
     msum[b] = 0;
   }
+  // the first block sums are loaded before the chunk partials are used, so
+  // that both reads share one round trip
+  constexpr int PRE = 4;
+  float bpre[PRE];
+#pragma unroll
+  for (int e = 0; e < PRE; ++e) {
+    const int j = tid + 256 * e;
+    bpre[e] = j < nb ? bsum[(size_t)h * nb + j] : 0.0f;
+  }
   // softmax over all strides from the chunks' (max, exp-sum), every wave alike
   const float* zp = zpart + (size_t)h * nchunk * 2;
   float M = -INFINITY;
@@ -570,9 +579,9 @@ __global__ void __launch_bounds__(256) decode_select_kernel(const float* __restr
 
   // masses, their fixed-point total and the first digit's histogram
   unsigned long long fsum = 0;
-  for (int j = tid; j < nb; j += 256) {
+  auto block_mass = [&](int j, float b) {
     const int ch = (j * r) >> 8;
-    float m = bsum[(size_t)h * nb + j] * __builtin_amdgcn_exp2f(zp[2 * ch] - M) * inv_s;
+    float m = b * __builtin_amdgcn_exp2f(zp[2 * ch] - M) * inv_s;
     mass[(size_t)h * nb + j] = m;
     m = m > 0.0f ? m : 0.0f;  // NaN and negative count as 0
     mm[j] = m;
@@ -583,7 +592,11 @@ __global__ void __launch_bounds__(256) decode_select_kernel(const float* __restr
       atomicAdd(&cnt[d], 1u);
       atomicAdd(&msum[d], f);
     }
-  }
+  };
+#pragma unroll
+  for (int e = 0; e < PRE; ++e)
+    if (tid + 256 * e < nb) block_mass(tid + 256 * e, bpre[e]);
+  for (int j = tid + 256 * PRE; j < nb; j += 256) block_mass(j, bsum[(size_t)h * nb + j]);
   if (all) {
     for (int j = tid; j < nb; j += 256) {
       out[j] = j;
