@@ -206,26 +206,24 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
       f32x16 acc = {};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) acc = Mfma<T>::acc(kf[c], qf[ct][c], acc);
+      // the maximum on the raw scores (cscale > 0), the scale folded into the exponent's FMA
       float tmax = -INFINITY;
       if (whole) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          acc[v] *= cscale;
-          tmax = fmaxf(tmax, acc[v]);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[v]);
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int t = tile * 32 + out_row(v, half);
-          acc[v] = (t <= lim[ct]) ? acc[v] * cscale : -INFINITY;
+          if (t > lim[ct]) acc[v] = -INFINITY;
           tmax = fmaxf(tmax, acc[v]);
         }
       }
       if (tmax > -INFINITY) {
-        const float mnew = fmaxf(mrun[ct], tmax);
+        const float mnew = fmaxf(mrun[ct], tmax * cscale);
         float sum = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sum += exp2_approx(acc[v] - mnew);
+        for (int v = 0; v < 16; ++v) sum += exp2_approx(__builtin_fmaf(acc[v], cscale, -mnew));
         lrun[ct] = lrun[ct] * exp2_approx(mrun[ct] - mnew) + sum;
         mrun[ct] = mnew;
       }
