@@ -321,8 +321,8 @@ def main():
             raise SystemExit("hbm_read is not built: run python -m dynamic_block_sparse_rr_amd.build")
         sys.exit(subprocess.run([probe, str(w.L), str(w.Hkv)]).returncode)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the operator is single-device; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the operator runs on a single device "
+              "(sharding it across GPUs is a design note, not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
