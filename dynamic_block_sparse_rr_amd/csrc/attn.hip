@@ -4,14 +4,18 @@
 // Inference" reports about half of the blocks computed).
 //
 // bfloat16 path (the hot kernel)
-//   transpose_v  V [L][Hkv][d] -> Vt [Hkv][nb][d][B]: each key block becomes a
-//                contiguous 2*B*d-byte tile whose rows are head-dim channels
-//                and whose columns are the block's keys (permuted inside every
-//                group of 16, see key_of_pos). One HBM pass over V.
+//   transpose_v  V [L][Hkv][d] -> Vt [Hkv][nb][B/8][d][8]: each key block
+//                becomes a contiguous 2*B*d-byte tile of 16-byte chunks, chunk
+//                (c, e) holding channel e at the block's positions 8c..8c+7
+//                (keys permuted inside every group of 16, see key_of_pos),
+//                chunk-major so that the copy into LDS is a straight copy and
+//                every MFMA operand read is one contiguous run. One HBM pass
+//                over V.
 //   attn_bf16    one workgroup of B/32 waves per (query head h, query block i);
 //                wave w owns 32 query rows. Per selected key block j:
-//                  K tile and Vt tile staged in LDS (16-byte chunks, XOR
-//                  swizzled by row so the MFMA operand reads are conflict-free);
+//                  K tile and Vt tile staged in LDS (K as 16-byte chunks XOR
+//                  swizzled by row, Vt chunk-major as stored, so the MFMA
+//                  operand reads are conflict-free);
 //                  S^T = K Q^T on v_mfma_f32_32x32x16_bf16: each lane ends up
 //                  owning one query and 64 of its keys (the other lane half
 //                  owns the other 64), so the online softmax (running max and
@@ -85,7 +89,7 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
   uint16_t* dst = reinterpret_cast<uint16_t*>(vt) + ((size_t)g * nb + j) * D * BLK;
   constexpr int OCH = BLK / 8;  // 16-byte chunks per channel row
   for (int n = threadIdx.x; n < D * OCH; n += 256) {
-    const int e = n / OCH, c = n % OCH;
+    const int e = n % D, c = n / D;  // consecutive threads, consecutive chunks of the tile
     u32x4 w;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -93,7 +97,7 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
       const int k0 = (p0 & ~15) + key_of_pos(p0 & 15), k1 = (p1 & ~15) + key_of_pos(p1 & 15);
       w[t] = (uint32_t)tile[k0][e] | ((uint32_t)tile[k1][e] << 16);
     }
-    *reinterpret_cast<u32x4*>(dst + (size_t)e * BLK + c * 8) = w;
+    *reinterpret_cast<u32x4*>(dst + ((size_t)c * D + e) * 8) = w;
   }
 }
 
@@ -128,12 +132,11 @@ struct AttnCtx {
   static constexpr int TILE = BLK * D * 2;           // bytes of one K or Vt tile
   static constexpr int NDMA = TILE / (NTHR * 16);    // 16-byte copies per thread per tile
   static constexpr int KCH = D / 8;                  // 16-byte chunks per K row
-  static constexpr int VCH = BLK / 8;                // 16-byte chunks per Vt row
   uint8_t* lds_k;
   uint8_t* lds_v;
   uint32_t koff, voff;    // this thread's copy source for copy 0, relative to a tile base
   uint32_t kstep, vstep;  // source distance between consecutive copies (bytes)
-  int kro, vro;          // operand read offsets for chunk 0 (XOR in the chunk index)
+  int kro, vro;          // operand read offsets for chunk 0 (K: XOR in the chunk index; Vt: add)
   int wave, qr, half;
   float cscale;
 };
@@ -262,7 +265,7 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   constexpr int NPV = NT * MT * 2;
   auto vread = [&](int k) {
     const int t = k / (MT * 2), r = k % (MT * 2);
-    return *reinterpret_cast<const bf16x8*>(cx.lds_v + t * 32 * BLK * 2 + (cx.vro ^ (((r >> 1) * 4 + 2 * (r & 1)) << 4)));
+    return *reinterpret_cast<const bf16x8*>(cx.lds_v + cx.vro + (2 * r * D + t * 32) * 16);
   };
 #pragma unroll
   for (int k = 0; k < LA; ++k) ring[k] = vread(k);
@@ -275,7 +278,7 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   }
   // every wave is done with the V buffer: the next block's V may land in it
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (has_next) copy_tile<D, BLK, AttnCtx<D, BLK>::VCH>(cx, next_v, cx.voff, cx.vstep, cx.lds_v);
+  if (has_next) copy_tile<D, BLK, 1>(cx, next_v, cx.voff, cx.vstep, cx.lds_v);
 }
 
 template <int D, int BLK>
@@ -285,7 +288,6 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
     int Hq, int Hkv, int nb, int causal, float cscale, int L) {
   typedef AttnCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
-  constexpr int VCH = C::VCH;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v[C::TILE];
 
@@ -305,25 +307,26 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   cx.qr = cx.wave * 32 + n32;  // query row inside the block
   const int x = i * BLK + cx.qr;
 
-  // Tiles live in LDS as rows of 16-byte chunks, chunk c of row r stored at
+  // K tiles live in LDS as rows of 16-byte chunks, chunk c of row r stored at
   // position c ^ (r mod chunks-per-row), so the 32 rows one MFMA operand read
   // touches fall in distinct banks. Copies write LDS linearly (lane l of a
   // wave's copy lands at 16*l), so each thread fetches the global chunk that
   // belongs at its position: a base offset, a fixed step per copy, and a
-  // per-copy XOR of the chunk (see copy_tile).
-  static_assert(C::NTHR % KCH == 0 && C::NTHR % VCH == 0, "copy rows must advance evenly");
+  // per-copy XOR of the chunk (see copy_tile). Vt tiles are chunk-major in
+  // HBM already: an operand read (32 channels of one chunk column) is one
+  // contiguous run, and the copy is straight.
+  static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
   {
     const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
     cx.koff = (kr * Hkv * D + kc * 8) * 2;
     cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
-    const int vr = tid / VCH, vc = (tid % VCH) ^ (vr & (VCH - 1));
-    cx.voff = (vr * BLK + vc * 8) * 2;
-    cx.vstep = (C::NTHR / VCH) * BLK * 2;
+    cx.voff = tid * 16;  // Vt tiles are copied as stored
+    cx.vstep = C::NTHR * 16;
   }
   // An operand read of chunk c in a row r = 32*m + n32 is at r*rowbytes +
   // 16*(c ^ (n32 mod chunks)); with c = 2*cc + half that is kro ^ (32*cc).
   cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
-  cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
+  cx.vro = (cx.half * D + n32) * 16;
 
   bf16x8 qf[C::DK];
   if (x < L) {
@@ -359,7 +362,7 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   int j = cnt > 0 ? min(max(lst[0], 0), jmax) : 0;
   if (cnt > 0) {
     copy_tile<D, BLK, KCH>(cx, krsrc(j), cx.koff, cx.kstep, lds_k);
-    copy_tile<D, BLK, VCH>(cx, vrsrc(j), cx.voff, cx.vstep, lds_v);
+    copy_tile<D, BLK, 1>(cx, vrsrc(j), cx.voff, cx.vstep, lds_v);
   }
   // Lists are ascending, so only the last entry can need a mask (the causal
   // diagonal block, or a short last block): the loop never masks, the peeled
@@ -421,10 +424,11 @@ struct PairCtx {
   static constexpr int TILE = BLK * D * 2;           // bytes of one K or Vt tile
   static constexpr int NDMA = TILE / (NTHR * 16);    // 16-byte copies per thread per tile
   static constexpr int KCH = D / 8;                  // 16-byte chunks per K row
-  static constexpr int VCH = BLK / 8;                // 16-byte chunks per Vt row
+  static constexpr int VBIAS = 2 * TILE;             // LDS offset of the first Vt stage (after the K stages)
   uint32_t koff, voff;    // this thread's copy source for copy 0, relative to a tile base
   uint32_t kstep, vstep;  // source distance between consecutive copies (bytes)
-  int kro, vro;           // operand read offsets for chunk 0 (XOR in the chunk index)
+  int kro, vro;           // operand read offsets for chunk 0 (K: XOR in the chunk index; Vt: add)
+  int vro_hi;             // vro + VBIAS, opaque to the optimizer (see the kernel)
   int wave, qr, half;
   float cscale;
 };
@@ -444,6 +448,64 @@ __device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, __amdgpu_bu
         reinterpret_cast<__attribute__((address_space(3))) void*>(
             reinterpret_cast<uintptr_t>(dst + (n * C::NTHR + cx.wave * 64) * 16)),
         16, (int)(n * step + (off ^ (((n * RPC) & (CH - 1)) << 4))), 0, 0, 0);
+}
+
+// Online softmax of one key block for one wave, in base 2 with the scale
+// folded into cscale: running maximum and sum updated, O rescaled when the
+// maximum grew, P rounded to bf16 in the B-operand layout of O^T += Vt P^T.
+// MASK: keys with index > klim inside the block get probability zero.
+template <int D, int BLK, bool MASK>
+__device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (&sacc)[BLK / 32],
+                                             f32x16 (&oacc)[D / 32], float& mrow, float& lrow,
+                                             bf16x8 (&pf)[BLK / 32][2], int klim) {
+  constexpr int MT = BLK / 32;
+  constexpr int NT = D / 32;
+  if (MASK) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
+        if (key > klim) sacc[mt][v] = -INFINITY;
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  const float mnew = fmaxf(mrow, tmax * cx.cscale);
+  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
+    const float alpha = exp2_approx(mrow - mnew);
+    lrow *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+  }
+  mrow = mnew;
+  // P in bf16 (B operand of O^T += Vt P^T); the row sum adds exactly the
+  // rounded values the MFMA multiplies, two at a time
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
+        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
+        w[e] = pack_bf16x2(p0, p1);
+        ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
+      }
+      pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+    }
+  }
+  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
 // One key block for one wave, operands already in LDS (no barriers inside).
@@ -483,58 +545,13 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
-  if (MASK) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
-        if (key > klim) sacc[mt][v] = -INFINITY;
-      }
-  }
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  }
-  const float mnew = fmaxf(mrow, tmax * cx.cscale);
-  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
-    const float alpha = exp2_approx(mrow - mnew);
-    lrow *= alpha;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-  }
-  mrow = mnew;
-  // P in bf16 (B operand of O^T += Vt P^T); the row sum adds exactly the
-  // rounded values the MFMA multiplies, two at a time
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 pf[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
-        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
-        w[e] = pack_bf16x2(p0, p1);
-        ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
-      }
-      pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
-    }
-  }
-  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  pair_softmax<D, BLK, MASK>(cx, sacc, oacc, mrow, lrow, pf, klim);
   // O^T += Vt P^T
   constexpr int NPV = NT * MT * 2;
   auto vread = [&](int k) {
     const int t = k / (MT * 2), r = k % (MT * 2);
-    return *reinterpret_cast<const bf16x8*>(lds_v + t * 32 * BLK * 2 + (cx.vro ^ (((r >> 1) * 4 + 2 * (r & 1)) << 4)));
+    return *reinterpret_cast<const bf16x8*>(lds_v + (cx.vro_hi - C::VBIAS) + (2 * r * D + t * 32) * 16);
   };
 #pragma unroll
   for (int k = 0; k < LA; ++k) ring[k] = vread(k);
@@ -578,7 +595,6 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     int Hq, int Hkv, int nb, int causal, float cscale, int L) {
   typedef PairCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
-  constexpr int VCH = C::VCH;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[C::TILE];
@@ -604,17 +620,24 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   const bool active = slot == 0 || hasB;  // a lone last head leaves slot 1 idle
   const int x = i * BLK + cx.qr;
 
-  static_assert(C::NTHR % KCH == 0 && C::NTHR % VCH == 0, "copy rows must advance evenly");
+  static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
   {
     const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
     cx.koff = (kr * Hkv * D + kc * 8) * 2;
     cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
-    const int vr = tid / VCH, vc = (tid % VCH) ^ (vr & (VCH - 1));
-    cx.voff = (vr * BLK + vc * 8) * 2;
-    cx.vstep = (C::NTHR / VCH) * BLK * 2;
+    cx.voff = tid * 16;  // Vt tiles are copied as stored
+    cx.vstep = C::NTHR * 16;
   }
   cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
-  cx.vro = n32 * BLK * 2 + (((cx.half) ^ (n32 & (VCH - 1))) << 4);
+  cx.vro = (cx.half * D + n32) * 16;
+  // The Vt stages follow the two K stages in LDS (at 64 and 96 KiB for d =
+  // 128), beyond the 16-bit offset field of ds_read_b128. Written as lds_v +
+  // vro + offset, every read costs a VALU add (the stage base folds into the
+  // constant, which then does not fit); written as lds_v + (vro_hi - VBIAS) +
+  // offset with vro_hi opaque, the constants cancel against the base and each
+  // read is vro_hi plus an immediate. Either form addresses the same bytes.
+  cx.vro_hi = cx.vro + C::VBIAS;
+  asm volatile("" : "+v"(cx.vro_hi));
 
   bf16x8 qf[C::DK];
   if (active && x < L) {
@@ -663,7 +686,7 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   auto copy_block = [&](int jb_, uint8_t* kdst, uint8_t* vdst) {
     const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jb_ * kstride, k_bytes, kbytes);
     pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jb_ * kstride, kb), cx.koff, cx.kstep, kdst);
-    pair_copy<D, BLK, VCH>(cx, tile_rsrc(vg + (size_t)jb_ * C::TILE, C::TILE), cx.voff, cx.vstep, vdst);
+    pair_copy<D, BLK, 1>(cx, tile_rsrc(vg + (size_t)jb_ * C::TILE, C::TILE), cx.voff, cx.vstep, vdst);
   };
   int j = min(ja, jb);
   if (j <= jlast) copy_block(j, lds_k0, lds_v0);
@@ -728,13 +751,295 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   }
 }
 
-// Variant switch for measurement: RR_ATTN_PAIR=0 selects the one-head-per-workgroup kernel.
+// ------------------------------------------------------------------ bf16 attention, head pairs in ping-pong
+
+// The head-pair workgroup above runs its two waves per SIMD in step: both
+// issue their S = K Q^T MFMAs, then both run the softmax on the VALU while
+// the matrix unit idles, then both issue O += P V. Here the block is split
+// in two half-steps, each closed by a workgroup barrier, and the two heads
+// take opposite roles in them:
+//
+//   half-step 2n    head A: O += P(n-1) V(n-1), S(n) = K(n) Q^T   (MFMA)
+//                   head B: softmax(n-1)                            (VALU)
+//   half-step 2n+1  head A: softmax(n)
+//                   head B: O += P(n-1) V(n-1), S(n) = K(n) Q^T
+//
+// so the matrix unit of every SIMD is fed by one of its two waves at a time
+// while the other computes exponentials. Tiles: K(n) and V(n-1) are read in
+// half-steps 2n and 2n+1; the copies of K(n+1) and V(n) are issued at the
+// start of half-step 2n into the stages that held K(n-1) and V(n-2) (last
+// read in half-step 2n-1) and have landed at the end of half-step 2n+1. A
+// head that did not select block n skips its MFMAs and softmax for it; the
+// barriers and copies are the same for every wave.
+
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
+// S^T = K Q^T for one wave: the k-step outer and the key subtile inner, so
+// consecutive MFMAs feed different accumulators.
+template <int D, int BLK>
+__device__ __forceinline__ void pp_qk(const PairCtx<D, BLK>& cx, const uint8_t* lds_k, const bf16x8 (&qf)[D / 16],
+                                      f32x16 (&sacc)[BLK / 32]) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int MT = C::MT;
+  constexpr int DK = C::DK;
+  constexpr int LA = 4;
+  constexpr int NQK = MT * DK;
+  auto kread = [&](int k) {
+    const int cc = k / MT, mt = k % MT;
+    return *reinterpret_cast<const bf16x8*>(lds_k + mt * 32 * D * 2 + (cx.kro ^ (cc << 5)));
+  };
+  bf16x8 ring[LA];
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = kread(k);
+#pragma unroll
+  for (int k = 0; k < NQK; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NQK) ring[k % LA] = kread(k + LA);
+    const int cc = k / MT, mt = k % MT;
+    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc ? sacc[mt] : f32x16{}, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
+#pragma unroll
+  for (int k = 0; k < NQK - LA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+}
+
+// O^T += Vt P^T for one wave: the key step outer and the channel tile inner.
+template <int D, int BLK>
+__device__ __forceinline__ void pp_pv(const PairCtx<D, BLK>& cx, const uint8_t* lds_v, const bf16x8 (&pf)[BLK / 32][2],
+                                      f32x16 (&oacc)[D / 32]) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int MT = C::MT;
+  constexpr int NT = C::NT;
+  constexpr int LA = 4;
+  constexpr int NPV = NT * MT * 2;
+  auto vread = [&](int k) {
+    const int r = k / NT, t = k % NT;
+    return *reinterpret_cast<const bf16x8*>(lds_v + (cx.vro_hi - C::VBIAS) + (2 * r * D + t * 32) * 16);
+  };
+  bf16x8 ring[LA];
+#pragma unroll
+  for (int k = 0; k < LA; ++k) ring[k] = vread(k);
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) {
+    const bf16x8 a = ring[k % LA];
+    if (k + LA < NPV) ring[k % LA] = vread(k + LA);
+    const int r = k / NT, t = k % NT;
+    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r >> 1][r & 1], oacc[t], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 1);
+#pragma unroll
+  for (int k = 0; k < NPV - LA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
+}
+
+template <int D, int BLK>
+__global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pp_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
+    const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
+    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
+  typedef PairCtx<D, BLK> C;
+  constexpr int KCH = C::KCH;
+  constexpr int MT = C::MT;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  C cx;
+  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = cx.wave / C::WPH;  // 0: head A (MFMAs in even half-steps), 1: head B
+  const int n32 = lane & 31;
+  cx.half = lane >> 5;
+  cx.qr = (cx.wave % C::WPH) * 32 + n32;
+  cx.cscale = cscale;
+  const int G = Hq / Hkv;
+  const int npairs = (G + 1) / 2;
+  int g, i, p;
+  pair_item(blockIdx.x, Hkv, nb, npairs, g, i, p);
+  const int hA = g * G + 2 * p;
+  const bool hasB = 2 * p + 1 < G;
+  const int hB = hA + 1;
+  const int h = slot ? hB : hA;
+  const bool active = slot == 0 || hasB;  // a lone last head leaves slot 1 idle
+  const int x = i * BLK + cx.qr;
+
+  static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
+  {
+    const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
+    cx.koff = (kr * Hkv * D + kc * 8) * 2;
+    cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
+    cx.voff = tid * 16;  // Vt tiles are copied as stored
+    cx.vstep = C::NTHR * 16;
+  }
+  cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
+  cx.vro = (cx.half * D + n32) * 16;
+  cx.vro_hi = cx.vro + C::VBIAS;  // see attn_bf16_pair_kernel
+  asm volatile("" : "+v"(cx.vro_hi));
+
+  bf16x8 qf[C::DK];
+  if (active && x < L) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
+  } else {
+#pragma unroll
+    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
+  }
+
+  // the two block lists, merged on the fly (all values wave-uniform)
+  const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
+  const int jlast = causal ? i : nb - 1;  // largest admissible key block
+  // the masked block, if any: the causal diagonal, else a short last block
+  const int jdiag = causal ? i : (ltail < BLK ? nb - 1 : nb);
+  const int klim = causal ? cx.qr : ltail - 1;
+  const size_t rowA = (size_t)hA * nb + i, rowB = (size_t)hB * nb + i;
+  const int cntA = min(max(row_count[rowA], 0), nb);
+  const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
+  const int32_t* la = col_idx + rowA * nb;
+  const int32_t* lb = col_idx + rowB * nb;
+  constexpr int kNone = 1 << 30;
+  int ia = 0, ib = 0;
+  int ja = cntA > 0 ? min(max(la[0], 0), jlast) : kNone;
+  int jb = cntB > 0 ? min(max(lb[0], 0), jlast) : kNone;
+
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
+  const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
+
+  f32x16 oacc[C::NT];
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
+  float mrow = -INFINITY, lrow = 0.0f;
+  f32x16 sacc[MT];
+  bf16x8 pf[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pf[mt][0] = pf[mt][1] = bf16x8{};
+
+  constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+  const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
+  auto copy_k = [&](int jj, uint8_t* dst) {
+    const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jj * kstride, k_bytes, kbytes);
+    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jj * kstride, kb), cx.koff, cx.kstep, dst);
+  };
+  auto copy_v = [&](int jj, uint8_t* dst) {
+    pair_copy<D, BLK, 1>(cx, tile_rsrc(vg + (size_t)jj * C::TILE, C::TILE), cx.voff, cx.vstep, dst);
+  };
+  int j = min(ja, jb);  // block n of the merged list (> jlast: the list is done)
+  if (j <= jlast) copy_k(j, lds_k0);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+
+  // Block n with K(n) in kc and V(n-1) in vp; K(n+1) is copied to kn and V(n)
+  // to vc. Returns false after the step past the last block (which only
+  // finishes the last P V). SLOT is this wave's head: 0 issues its MFMAs in
+  // the first half-step, 1 in the second.
+  auto run = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    bool sel_prev = false;  // this wave's head selected block n-1
+    auto mfma_phase = [&](bool sel, bool diag, const uint8_t* kc, const uint8_t* vp) __attribute__((always_inline)) {
+      if (sel_prev) pp_pv<D, BLK>(cx, vp, pf, oacc);
+      if (sel) {
+        pp_qk<D, BLK>(cx, kc, qf, sacc);
+        if (diag) {  // keys past the lane's limit get score -inf (probability zero)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
+              if (key > klim) sacc[mt][v] = -INFINITY;
+            }
+        }
+      }
+    };
+    auto step = [&](const uint8_t* kc, uint8_t* kn, const uint8_t* vp, uint8_t* vc) __attribute__((always_inline)) {
+      const bool have = j <= jlast;
+      const bool selA = have && ja == j, selB = have && jb == j;
+      if (selA) {
+        ++ia;
+        ja = ia < cntA ? min(max(la[ia], 0), jlast) : kNone;
+      }
+      if (selB) {
+        ++ib;
+        jb = ib < cntB ? min(max(lb[ib], 0), jlast) : kNone;
+      }
+      const int jn = min(ja, jb);
+      const bool sel = SLOT ? selB : selA;
+      const bool diag = have && j == jdiag;
+      if (jn <= jlast) copy_k(jn, kn);
+      if (have) copy_v(j, vc);
+      // half-step 2n
+      if (SLOT == 0)
+        mfma_phase(sel, diag, kc, vp);
+      else if (sel_prev)
+        pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+      __builtin_amdgcn_s_barrier();
+      // half-step 2n+1
+      if (SLOT == 0) {
+        if (sel) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+      } else {
+        mfma_phase(sel, diag, kc, vp);
+      }
+      // this block's reads are done and the copies issued at its start have landed
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __builtin_amdgcn_s_barrier();
+      sel_prev = sel;
+      j = jn;
+      return have;
+    };
+    // two blocks per trip, so that each stage's LDS objects are known at compile time
+    while (step(lds_k0, lds_k1, lds_v1, lds_v0) && step(lds_k1, lds_k0, lds_v0, lds_v1)) {
+    }
+  };
+  if (slot == 0)
+    run(IntConst<0>{});
+  else
+    run(IntConst<1>{});
+
+  if (!active || x >= L) return;
+  const float ltot = lrow + __shfl_xor(lrow, 32);
+  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int e = t * 32 + 8 * v4 + 4 * cx.half;
+      u32x2 w;
+      w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
+      w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(dst + e) = w;
+    }
+  }
+}
+
+// Variant switch: RR_ATTN_PP=0 selects the head-pair kernel without ping-pong
+// (read at every launch, so that one process can run and test both).
+bool attn_pp_enabled() {
+  const char* e = getenv("RR_ATTN_PP");
+  return !(e && e[0] == '0');
+}
+
+// Variant switch: RR_ATTN_PAIR=0 selects the one-head-per-workgroup kernel
+// (read at every launch, like RR_ATTN_PP).
 bool attn_pair_enabled() {
-  static const bool on = [] {
-    const char* e = getenv("RR_ATTN_PAIR");
-    return !(e && e[0] == '0');
-  }();
-  return on;
+  const char* e = getenv("RR_ATTN_PAIR");
+  return !(e && e[0] == '0');
 }
 
 // ------------------------------------------------------------------ fp32 attention
@@ -831,6 +1136,15 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
     const int G = g.Hq / g.Hkv;
     if (g.B == 128 && G >= 2 && attn_pair_enabled()) {
       const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
+      if (attn_pp_enabled()) {
+        if (g.d == 128)
+          attn_bf16_pp_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                              g.nb, g.causal, cscale, g.L);
+        else
+          attn_bf16_pp_kernel<64, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                             g.nb, g.causal, cscale, g.L);
+        return hipGetLastError();
+      }
       if (g.d == 128)
         attn_bf16_pair_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
                                                               g.nb, g.causal, cscale, g.L);
