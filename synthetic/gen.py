@@ -81,6 +81,9 @@ WORKLOADS = {
         Workload("llama8b_L16k", 16384, 32, 8, 128, "bf16", 128, 16, (0.9,), 1, "llm", 16),
         Workload("llama8b_L32k", 32768, 32, 8, 128, "bf16", 128, 16, (0.85, 0.9, 0.95), 2, "llm", 32),
         Workload("llama8b_L128k", 131072, 32, 8, 128, "bf16", 128, 16, (0.9,), 3, "llm", 64),
+        # One GPU's share of the 128K layer split by KV head over 8 GPUs: 4 query
+        # heads and their one KV head at full length (same recipe and seed).
+        Workload("llama8b_L128k_tp8_share", 131072, 4, 1, 128, "bf16", 128, 16, (0.9,), 3, "llm", 64),
         # Video-LMM-shaped layer: 28 query heads, 4 KV heads.
         Workload("video_L64k", 65536, 28, 4, 128, "bf16", 128, 16, (0.9,), 4, "video"),
     ]
