@@ -28,6 +28,14 @@
 //                first, the G query heads sharing a KV head adjacent and on
 //                the same XCD (dispatch is round-robin over the 8 XCDs), so
 //                K/V tiles are reused from that XCD's L2.
+//   attn_bf16_pair  two query heads of one KV head per workgroup (two waves
+//                per SIMD, one per head), walking the merged block list of
+//                both heads: each K/Vt tile is copied once for both, tiles
+//                double-buffered with one barrier per block.
+//   attn_bf16_pp the default for B = 128 and G >= 2: the head-pair workgroup
+//                in ping-pong, each block split in two half-steps so that one
+//                head's waves issue their MFMAs while the other head's run
+//                the softmax (see the kernel).
 // float32 path: a plain kernel (one thread per query row, K/V tiles in LDS,
 // online softmax in registers).
 #include <hip/hip_runtime.h>
