@@ -106,9 +106,15 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  * ascending, < nb, and (causal) <= its query block index: rows breaking this
  * give undefined output (the library does not read lists back to the host).
  *   q, k, v     device inputs in p->dtype; out: device output [L][Hq][d] in p->dtype.
- *   ws          device workspace (holds a key-major copy of V and the row schedule).
+ *   ws          device workspace (bf16: holds a copy of V re-laid out as one
+ *               channels-by-keys tile per key block).
  * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
  * p->S and p->tau are not used but must be valid.
+ * Kernel choice (bf16, B = 128, two or more query heads per KV head): two
+ * query heads per workgroup in a ping-pong schedule. The environment
+ * variables RR_ATTN_PP=0 (head pairs without ping-pong) and RR_ATTN_PAIR=0
+ * (one head per workgroup), read at every call, select the other kernels for
+ * measurement; results agree with the default within bf16 rounding.
  */
 rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* row_count, const int32_t* col_idx, void* out,
