@@ -303,3 +303,17 @@ def test_attention_rejects_bad_lists():
     ci2[1, 0, 0] = 2  # beyond the diagonal
     with pytest.raises(ValueError):
         oracle.attention(q, k, k, rc2, ci2, B=B)
+
+
+def test_identical_keys_give_running_mean_of_values():
+    """Closed form: with every key equal, each causal row's softmax is uniform
+    over its visible keys, so the output is the running mean of the values."""
+    L, Hq, Hkv, d, B = 200, 4, 2, 16, 32
+    q = _rand((L, Hq, d), 11, scale=3.0)
+    k = np.broadcast_to(_rand((1, 1, d), 12), (L, Hkv, d)).copy()
+    v = _rand((L, Hkv, d), 13)
+    rc, ci = oracle.full_lists(L, Hq, B)
+    got = oracle.attention(q, k, v, rc, ci, B=B)
+    mean = np.cumsum(v.astype(np.float64), axis=0) / np.arange(1, L + 1)[:, None, None]
+    for h in range(Hq):
+        np.testing.assert_allclose(got[:, h, :], mean[:, h // (Hq // Hkv), :], rtol=0, atol=1e-12)
