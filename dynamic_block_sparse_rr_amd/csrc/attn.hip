@@ -112,22 +112,23 @@ __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restri
 // ------------------------------------------------------------------ bf16 attention
 
 // Maps the launch index to (query head, query block): query blocks in
-// decreasing order (causal rows get longer with i), the G heads of one KV
-// head on one XCD in consecutive dispatch slots.
-__device__ __forceinline__ void work_item(int x, int Hq, int Hkv, int nb, int& h, int& i) {
+// decreasing order (causal rows get longer with i), the heads of one KV head
+// on one XCD in consecutive dispatch slots. The launch covers heads hbase ..
+// hbase + hcount - 1 of every KV head (all G of them, or one).
+__device__ __forceinline__ void work_item(int x, int Hq, int Hkv, int nb, int hbase, int hcount, int& h, int& i) {
   const int G = Hq / Hkv;
   const int nunits = Hkv * nb;
   int u, hh;
   if ((nunits & 7) == 0) {
     const int xcd = x & 7, t = x >> 3;
-    hh = t % G;
-    u = (t / G) * 8 + xcd;
+    hh = t % hcount;
+    u = (t / hcount) * 8 + xcd;
   } else {
-    u = x / G;
-    hh = x % G;
+    u = x / hcount;
+    hh = x % hcount;
   }
   i = nb - 1 - u / Hkv;
-  h = (u % Hkv) * G + hh;
+  h = (u % Hkv) * G + hbase + hh;
 }
 
 // Shared state of one workgroup of the bf16 kernel.
@@ -293,7 +294,7 @@ template <int D, int BLK>
 __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
+    int Hq, int Hkv, int nb, int causal, float cscale, int L, int hbase, int hcount) {
   typedef AttnCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_k[C::TILE];
@@ -309,7 +310,7 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   cx.half = lane >> 5;
   cx.cscale = cscale;
   int h, i;
-  work_item(blockIdx.x, Hq, Hkv, nb, h, i);
+  work_item(blockIdx.x, Hq, Hkv, nb, hbase, hcount, h, i);
   const int G = Hq / Hkv;
   const int g = h / G;
   cx.qr = cx.wave * 32 + n32;  // query row inside the block
@@ -850,7 +851,9 @@ __device__ __forceinline__ void pp_pv(const PairCtx<D, BLK>& cx, const uint8_t* 
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
 }
 
-template <int D, int BLK>
+// LONE_APART: with an odd group the last head of every KV head is left to
+// another launch (the one-head kernel), so only the full pairs are mapped.
+template <int D, int BLK, bool LONE_APART>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pp_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
@@ -873,7 +876,7 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   cx.qr = (cx.wave % C::WPH) * 32 + n32;
   cx.cscale = cscale;
   const int G = Hq / Hkv;
-  const int npairs = (G + 1) / 2;
+  const int npairs = LONE_APART ? G / 2 : (G + 1) / 2;
   int g, i, p;
   pair_item(blockIdx.x, Hkv, nb, npairs, g, i, p);
   const int hA = g * G + 2 * p;
@@ -1138,19 +1141,38 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
 #define RR_ATTN_CASE(DV, BV)                                                                      \
   if (g.d == DV && g.B == BV) {                                                                   \
     attn_bf16_kernel<DV, BV><<<grid, BV * 2, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq,    \
-                                                      g.Hkv, g.nb, g.causal, cscale, g.L);       \
+                                                      g.Hkv, g.nb, g.causal, cscale, g.L, 0,     \
+                                                      g.Hq / g.Hkv);                              \
     return hipGetLastError();                                                                     \
   }
     const int G = g.Hq / g.Hkv;
     if (g.B == 128 && G >= 2 && attn_pair_enabled()) {
       const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
       if (attn_pp_enabled()) {
-        if (g.d == 128)
-          attn_bf16_pp_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                              g.nb, g.causal, cscale, g.L);
-        else
-          attn_bf16_pp_kernel<64, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                             g.nb, g.causal, cscale, g.L);
+        // The full head pairs in ping-pong; with an odd group the last head of
+        // every KV head runs in the one-head kernel instead of leaving half of
+        // a pair workgroup idle.
+        const dim3 fgrid((unsigned)(g.Hkv * g.nb * (G / 2)));
+#define RR_PP_LAUNCH(DV, LONE)                                                                      \
+  attn_bf16_pp_kernel<DV, 128, LONE><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
+                                                            g.nb, g.causal, cscale, g.L)
+        if (g.d == 128) {
+          if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
+        } else {
+          if (G % 2) RR_PP_LAUNCH(64, true); else RR_PP_LAUNCH(64, false);
+        }
+#undef RR_PP_LAUNCH
+        if (G % 2 == 1) {
+          hipError_t e = hipGetLastError();
+          if (e != hipSuccess) return e;
+          const dim3 lgrid((unsigned)(g.Hkv * g.nb));
+          if (g.d == 128)
+            attn_bf16_kernel<128, 128><<<lgrid, 256, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                             g.nb, g.causal, cscale, g.L, G - 1, 1);
+          else
+            attn_bf16_kernel<64, 128><<<lgrid, 256, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
+                                                            g.nb, g.causal, cscale, g.L, G - 1, 1);
+        }
         return hipGetLastError();
       }
       if (g.d == 128)

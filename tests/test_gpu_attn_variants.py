@@ -9,7 +9,8 @@ the three outputs with each other within 1e-2 (the two head-pair kernels sum
 the same products in the same order; the one-head kernel forms the row sums
 from the unrounded probabilities).
 
-Shapes: an odd group (a lone last head leaves one half of a head pair idle),
+Shapes: an odd group (by default its last head runs in the one-head kernel
+next to the ping-pong pairs; the head-pair kernel leaves half a workgroup idle),
 a non-causal problem with a short last block, head dimension 64, and lists
 that the search produced, so heads of one pair select different blocks.
 """
