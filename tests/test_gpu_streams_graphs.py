@@ -59,8 +59,10 @@ def test_two_streams_at_once_match_sequential_calls():
     say("  two streams: both results bitwise equal to sequential calls")
 
 
-def test_prefill_graph_replays_match_eager_calls():
-    w = Workload("g", 4096, 8, 2, 128, "bf16", 128, 16, (0.9,), 33, "llm", 8)
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (6, 2)], ids=["group4", "group3_two_launches"])
+def test_prefill_graph_replays_match_eager_calls(hq, hkv):
+    # an odd group makes the attention two launches (head pairs, then the last heads)
+    w = Workload("g", 4096, hq, hkv, 128, "bf16", 128, 16, (0.9,), 33, "llm", 8)
     job = Job(w)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -74,7 +76,7 @@ def test_prefill_graph_replays_match_eager_calls():
     torch.cuda.synchronize()
     for rep in range(3):
         # new inputs in the captured buffers, then the replay, then the eager call on the same inputs
-        q, k, v = make_inputs(Workload("g", 4096, 8, 2, 128, "bf16", 128, 16, (0.9,), 40 + rep, "llm", 8))
+        q, k, v = make_inputs(Workload("g", 4096, hq, hkv, 128, "bf16", 128, 16, (0.9,), 40 + rep, "llm", 8))
         job.q.copy_(q.cuda())
         job.k.copy_(k.cuda())
         job.v.copy_(v.cuda())
