@@ -775,11 +775,13 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
 //
 // so the matrix unit of every SIMD is fed by one of its two waves at a time
 // while the other computes exponentials. Tiles: K(n) and V(n-1) are read in
-// half-steps 2n and 2n+1; the copies of K(n+1) and V(n) are issued at the
-// start of half-step 2n into the stages that held K(n-1) and V(n-2) (last
-// read in half-step 2n-1) and have landed at the end of half-step 2n+1. A
-// head that did not select block n skips its MFMAs and softmax for it; the
-// barriers and copies are the same for every wave.
+// half-steps 2n and 2n+1; the copies of K(n+1) and V(n) are issued in
+// half-step 2n (head B's waves before their softmax, head A's after their
+// MFMAs, so that no MFMA phase waits behind the copy issue) into the stages
+// that held K(n-1) and V(n-2) (last read in half-step 2n-1) and have landed
+// at the end of half-step 2n+1. A head that did not select block n skips its
+// MFMAs and softmax for it; the barriers and copies are the same for every
+// wave.
 
 template <int V>
 struct IntConst {
@@ -992,13 +994,21 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
       const int jn = min(ja, jb);
       const bool sel = SLOT ? selB : selA;
       const bool diag = have && j == jdiag;
-      if (jn <= jlast) copy_k(jn, kn);
-      if (have) copy_v(j, vc);
+      // each wave issues its share of the copies of K(n+1) and V(n) in
+      // half-step 2n where it is off the critical path: head B before its
+      // softmax, head A after its MFMAs
+      auto copies = [&]() __attribute__((always_inline)) {
+        if (jn <= jlast) copy_k(jn, kn);
+        if (have) copy_v(j, vc);
+      };
       // half-step 2n
-      if (SLOT == 0)
+      if (SLOT == 0) {
         mfma_phase(sel, diag, kc, vp);
-      else if (sel_prev)
-        pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+        copies();
+      } else {
+        copies();
+        if (sel_prev) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+      }
       __builtin_amdgcn_s_barrier();
       // half-step 2n+1
       if (SLOT == 0) {
