@@ -24,7 +24,7 @@ def problem_of(w: Workload, tau: float) -> rr.Problem:
     return rr.problem(w.L, w.Hq, w.Hkv, w.d, w.S, w.B, tau, w.causal, w.dtype)
 
 
-class GpuRun:
+class DeviceCase:
     """Inputs of one workload resident on the GPU plus the library's workspace."""
 
     def __init__(self, w: Workload, tau: float, inputs=None):

@@ -23,7 +23,7 @@ import pytest
 import oracle
 from synthetic.gen import Workload
 from tests import checker
-from tests.gpu_cases import GpuRun, say
+from tests.gpu_cases import DeviceCase, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def run_variant(run, env, rc, ci):
 @pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
 def test_attention_kernels_agree_with_oracle(w):
     say(f"case {w.name}")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     orc = oracle.search(run.q, run.k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=True)
     want = oracle.attention(run.q, run.k, run.v, orc.row_count, orc.col_idx, B=w.B, causal=w.causal)
     outs = {}

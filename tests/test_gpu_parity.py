@@ -16,7 +16,7 @@ import pytest
 import oracle
 from synthetic.gen import Workload, workload
 from tests import checker
-from tests.gpu_cases import GpuRun, sample_rows, say
+from tests.gpu_cases import DeviceCase, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,7 @@ def check_lists(w, tau, rc, ci, orc, rows=None):
 @pytest.mark.parametrize("w,tau", SMALL, ids=[c[0].name for c in SMALL])
 def test_small_shapes_full_parity(w, tau):
     say(f"case {w.name} tau={tau}")
-    run = GpuRun(w, tau)
+    run = DeviceCase(w, tau)
     rc, ci, mass = run.search(export_mass=True)
     orc = oracle_search(w, tau, run.q, run.k)
     np.testing.assert_allclose(mass, orc.mass, rtol=1e-4, atol=1e-6)
@@ -87,7 +87,7 @@ def test_small_shapes_full_parity(w, tau):
 
 def test_tau_one_equals_dense_attention():
     w = g("dense", 2048, 8, 2, 128, 16, 128, "bf16", kind="llm")
-    run = GpuRun(w, 1.0)
+    run = DeviceCase(w, 1.0)
     out, rc, ci = run.prefill()
     frc, fci = oracle.full_lists(w.L, w.Hq, w.B)
     np.testing.assert_array_equal(rc, frc)
@@ -101,7 +101,7 @@ def test_tau_one_equals_dense_attention():
 
 def test_runs_are_bitwise_deterministic():
     w = g("det", 4096, 8, 2, 128, 16, 128, "bf16", kind="llm")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     a = run.prefill()
     b = run.prefill()
     np.testing.assert_array_equal(a[1], b[1])
@@ -113,11 +113,11 @@ def test_runs_are_bitwise_deterministic():
 
 def test_query_independence_on_gpu():
     w = g("qi", 2048, 4, 2, 128, 16, 128, "bf16", kind="llm")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     rc, ci, _ = run.search(export_mass=False)
     q2 = run.q.clone()
     q2[(5 + 1) * w.B:] = -q2[(5 + 1) * w.B:]
-    run2 = GpuRun(w, 0.9, inputs=(q2, run.k, run.v))
+    run2 = DeviceCase(w, 0.9, inputs=(q2, run.k, run.v))
     rc2, ci2, _ = run2.search(export_mass=False)
     np.testing.assert_array_equal(rc[:, :6], rc2[:, :6])
     for h in range(w.Hq):
@@ -130,7 +130,7 @@ def test_query_independence_on_gpu():
 def _workload_case(name, tau, full_search, n_rows_sample=192, search_rows=None):
     w = workload(name)
     say(f"case {name} tau={tau} L={w.L}")
-    run = GpuRun(w, tau)
+    run = DeviceCase(w, tau)
     rc, ci, mass = run.search(export_mass=full_search)
     row_mask = None
     rows = None

@@ -15,7 +15,7 @@ import dynamic_block_sparse_rr_amd as rr
 import oracle
 from synthetic.gen import Workload, make_inputs
 from tests import checker
-from tests.gpu_cases import GpuRun, say
+from tests.gpu_cases import DeviceCase, say
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def tol(w):
 @pytest.mark.parametrize("w", RAGGED, ids=[w.name for w in RAGGED])
 def test_ragged_full_parity(w):
     say(f"ragged case {w.name} L={w.L} nb={w.nb} ns={w.ns}")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     rc, ci, mass = run.search(export_mass=True)
     orc = oracle.search(run.q, run.k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=w.dtype == "bf16")
     np.testing.assert_allclose(mass, orc.mass, rtol=1e-4, atol=1e-6)
@@ -74,7 +74,7 @@ def test_ragged_full_parity(w):
 def test_ragged_dense_equals_sdpa():
     # every block selected on a ragged length is plain causal attention
     w = g("dense_ragged", 1500, 4, 2, 128, 16, 128, "bf16", kind="llm")
-    run = GpuRun(w, 1.0)
+    run = DeviceCase(w, 1.0)
     out, rc, ci = run.prefill()
     frc, _ = oracle.full_lists(w.L, w.Hq, w.B)
     np.testing.assert_array_equal(rc, frc)
@@ -89,7 +89,7 @@ def test_ragged_dense_equals_sdpa():
 
 def test_threshold_per_head():
     w = g("per_head_tau", 2048, 8, 2, 128, 16, 128, "bf16", kind="llm")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     taus = np.array([0.5, 0.9, 0.75, 1.0, 0.3, 0.95, 0.85, 0.6], np.float32)
     td = torch.from_numpy(taus).cuda()
     rc = torch.empty((w.Hq, w.nb), dtype=torch.int32, device="cuda")
@@ -139,7 +139,7 @@ def test_varlen_batch_matches_single_sequences():
     for b, L in enumerate(lens):
         nb = nbs[b]
         w = Workload(f"seq{b}", L, 8, 2, 128, "bf16", 128, 16, (0.9,), 300 + b, "llm", 8)
-        one = GpuRun(w, 0.9, inputs=parts[b])
+        one = DeviceCase(w, 0.9, inputs=parts[b])
         o1, rc1, ci1 = one.prefill()
         rcb = rc[roff:roff + 8 * nb].reshape(8, nb)
         cib = ci[coff:coff + 8 * nb * nb].reshape(8, nb, nb)

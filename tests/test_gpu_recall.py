@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from synthetic.gen import Workload, workload
-from tests.gpu_cases import GpuRun, say
+from tests.gpu_cases import DeviceCase, say
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ SMALL = [
 @pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
 def test_recall_small_shapes_full(w):
     say(f"recall case {w.name}")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     rc, ci, _ = run.search(export_mass=False)
     got = run.recall(rc, ci)
     want = oracle.mass_recall(run.q, run.k, rc, ci, B=w.B, causal=w.causal)
@@ -60,7 +60,7 @@ def test_recall_small_shapes_full(w):
 def test_recall_workloads_sampled_rows(name, rows_i):
     w = workload(name)
     say(f"recall case {name}")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     rc, ci, _ = run.search(export_mass=False)
     got = run.recall(rc, ci)
     rng = np.random.default_rng(5)

@@ -25,7 +25,7 @@ import torch
 import oracle
 from synthetic.gen import Workload
 from tests import checker
-from tests.gpu_cases import GpuRun, say
+from tests.gpu_cases import DeviceCase, say
 from tests.test_gpu_attn_variants import VARIANTS, run_variant
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +73,7 @@ def dense_causal_lists(nb):
 def test_softmax_stress_all_kernels(case):
     say(f"case {case}")
     w = Workload(f"stress_{case}", L, HQ, HKV, D, "bf16", B, 16, (0.9,), 7, "gauss", 0, True)
-    run = GpuRun(w, 0.9, inputs=inputs(case))
+    run = DeviceCase(w, 0.9, inputs=inputs(case))
     rc, ci = dense_causal_lists(w.nb)
     want = oracle.attention(run.q, run.k, run.v, rc, ci, B=B, causal=True)
     assert np.all(np.isfinite(want))

@@ -62,7 +62,7 @@ def test_shared_lists_hold_at_least_the_per_head_recall():
 @pytest.mark.gpu
 @pytest.mark.parametrize("name", ["llm_g4", "gauss_g7", "llama8b_L128k"])
 def test_gpu_shared_lists_match_the_oracle(name):
-    from tests.gpu_cases import GpuRun, say
+    from tests.gpu_cases import DeviceCase, say
     if name == "llm_g4":
         w = Workload(name, 2048, 8, 2, 128, "bf16", 128, 16, (0.9,), 31, "llm", 8)
     elif name == "gauss_g7":
@@ -72,7 +72,7 @@ def test_gpu_shared_lists_match_the_oracle(name):
     import torch
     import dynamic_block_sparse_rr_amd as rr
     say(f"shared-mask case {name}")
-    run = GpuRun(w, 0.9)
+    run = DeviceCase(w, 0.9)
     rc, ci, _ = run.search(export_mass=False)
     src_rc = torch.from_numpy(rc).cuda()
     src_ci = torch.from_numpy(ci).cuda()
