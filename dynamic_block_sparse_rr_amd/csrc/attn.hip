@@ -35,7 +35,9 @@
 //   attn_bf16_pp the default for B = 128 and G >= 2: the head-pair workgroup
 //                in ping-pong, each block split in two half-steps so that one
 //                head's waves issue their MFMAs while the other head's run
-//                the softmax (see the kernel).
+//                the softmax (see the kernel). With an odd group the last
+//                head of each KV head pairs with itself over two adjacent
+//                query blocks (one per slot), so no slot is left idle.
 // float32 path: a plain kernel (one thread per query row, K/V tiles in LDS,
 // online softmax in registers).
 #include <hip/hip_runtime.h>
@@ -597,6 +599,27 @@ __device__ __forceinline__ void pair_item(int x, int Hkv, int nb, int npairs, in
   g = u % Hkv;
 }
 
+// Work item x of the ping-pong kernel for an odd group size G: unit u = (KV
+// head g, query blocks nb-1-2*pb and nb-2-2*pb) holds G items, slot `it`:
+// the G/2 head pairs of the upper block, the G/2 head pairs of the lower one,
+// and last the group's lone head over both blocks (one block per slot). Units
+// run longest rows first and, when their count allows, each XCD takes every
+// eighth unit, like pair_item.
+__device__ __forceinline__ void odd_item(int x, int Hkv, int npb, int G, int& g, int& pb, int& it) {
+  const int nunits = Hkv * npb;
+  int u;
+  if ((nunits & 7) == 0) {
+    const int xcd = x & 7, t = x >> 3;
+    it = t % G;
+    u = (t / G) * 8 + xcd;
+  } else {
+    u = x / G;
+    it = x % G;
+  }
+  pb = u / Hkv;
+  g = u % Hkv;
+}
+
 template <int D, int BLK>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pair_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
@@ -853,9 +876,10 @@ __device__ __forceinline__ void pp_pv(const PairCtx<D, BLK>& cx, const uint8_t* 
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
 }
 
-// LONE_APART: with an odd group the last head of every KV head is left to
-// another launch (the one-head kernel), so only the full pairs are mapped.
-template <int D, int BLK, bool LONE_APART>
+// ODD: the group size is odd and work items are decoded by odd_item (each
+// slot then has its own query block); otherwise by pair_item (both slots on
+// one query block).
+template <int D, int BLK, bool ODD>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pp_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
@@ -878,14 +902,34 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   cx.qr = (cx.wave % C::WPH) * 32 + n32;
   cx.cscale = cscale;
   const int G = Hq / Hkv;
-  const int npairs = LONE_APART ? G / 2 : (G + 1) / 2;
-  int g, i, p;
-  pair_item(blockIdx.x, Hkv, nb, npairs, g, i, p);
-  const int hA = g * G + 2 * p;
-  const bool hasB = 2 * p + 1 < G;
-  const int hB = hA + 1;
+  // slot 0 runs head hA on query block iA, slot 1 head hB on block iB
+  int g, hA, hB, iA, iB;
+  bool hasB = true;
+  if constexpr (!ODD) {  // G even: heads 2p and 2p+1 of one query block
+    int p;
+    pair_item(blockIdx.x, Hkv, nb, G / 2, g, iA, p);
+    iB = iA;
+    hA = g * G + 2 * p;
+    hB = hA + 1;
+  } else {
+    int pb, it;
+    odd_item(blockIdx.x, Hkv, (nb + 1) / 2, G, g, pb, it);
+    const int i0 = nb - 1 - 2 * pb, i1 = i0 - 1;
+    if (it < 2 * (G / 2)) {
+      iA = iB = it < G / 2 ? i0 : i1;
+      if (iA < 0) return;  // odd nb: the lowest unit has one block (uniform exit, before any barrier)
+      hA = g * G + 2 * (it % (G / 2));
+      hB = hA + 1;
+    } else {  // the lone head, block i0 in slot 0 and i1 (if any) in slot 1
+      hA = hB = g * G + G - 1;
+      iA = i0;
+      iB = i1;
+      hasB = i1 >= 0;
+    }
+  }
   const int h = slot ? hB : hA;
-  const bool active = slot == 0 || hasB;  // a lone last head leaves slot 1 idle
+  const int i = slot ? iB : iA;
+  const bool active = slot == 0 || hasB;
   const int x = i * BLK + cx.qr;
 
   static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
@@ -913,19 +957,23 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
 
   // the two block lists, merged on the fly (all values wave-uniform)
   const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
-  const int jlast = causal ? i : nb - 1;  // largest admissible key block
-  // the masked block, if any: the causal diagonal, else a short last block
-  const int jdiag = causal ? i : (ltail < BLK ? nb - 1 : nb);
+  // largest admissible key block of each slot's row, and of the merged walk (iA >= iB)
+  const int jlastA = causal ? iA : nb - 1;
+  const int jlastB = causal ? iB : nb - 1;
+  const int jlast = jlastA;
+  // each slot's masked block, if any: its causal diagonal, else a short last block
+  const int jdiagA = causal ? iA : (ltail < BLK ? nb - 1 : nb);
+  const int jdiagB = causal ? iB : (ltail < BLK ? nb - 1 : nb);
   const int klim = causal ? cx.qr : ltail - 1;
-  const size_t rowA = (size_t)hA * nb + i, rowB = (size_t)hB * nb + i;
+  const size_t rowA = (size_t)hA * nb + iA, rowB = (size_t)hB * nb + iB;
   const int cntA = min(max(row_count[rowA], 0), nb);
   const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
   const int32_t* la = col_idx + rowA * nb;
   const int32_t* lb = col_idx + rowB * nb;
   constexpr int kNone = 1 << 30;
   int ia = 0, ib = 0;
-  int ja = cntA > 0 ? min(max(la[0], 0), jlast) : kNone;
-  int jb = cntB > 0 ? min(max(lb[0], 0), jlast) : kNone;
+  int ja = cntA > 0 ? min(max(la[0], 0), jlastA) : kNone;
+  int jb = cntB > 0 ? min(max(lb[0], 0), jlastB) : kNone;
 
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
@@ -985,15 +1033,15 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
       const bool selA = have && ja == j, selB = have && jb == j;
       if (selA) {
         ++ia;
-        ja = ia < cntA ? min(max(la[ia], 0), jlast) : kNone;
+        ja = ia < cntA ? min(max(la[ia], 0), jlastA) : kNone;
       }
       if (selB) {
         ++ib;
-        jb = ib < cntB ? min(max(lb[ib], 0), jlast) : kNone;
+        jb = ib < cntB ? min(max(lb[ib], 0), jlastB) : kNone;
       }
       const int jn = min(ja, jb);
       const bool sel = SLOT ? selB : selA;
-      const bool diag = have && j == jdiag;
+      const bool diag = have && j == (SLOT ? jdiagB : jdiagA);
       // each wave issues its share of the copies of K(n+1) and V(n) in
       // half-step 2n where it is off the critical path: head B before its
       // softmax, head A after its MFMAs
@@ -1159,30 +1207,19 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
     if (g.B == 128 && G >= 2 && attn_pair_enabled()) {
       const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
       if (attn_pp_enabled()) {
-        // The full head pairs in ping-pong; with an odd group the last head of
-        // every KV head runs in the one-head kernel instead of leaving half of
-        // a pair workgroup idle.
-        const dim3 fgrid((unsigned)(g.Hkv * g.nb * (G / 2)));
-#define RR_PP_LAUNCH(DV, LONE)                                                                      \
-  attn_bf16_pp_kernel<DV, 128, LONE><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
-                                                            g.nb, g.causal, cscale, g.L)
+        // Even group: G/2 head pairs per (KV head, query block). Odd group: G
+        // items per (KV head, two query blocks), the lone head of the group
+        // paired with itself over the two blocks (odd_item).
+        const dim3 fgrid((unsigned)(G % 2 ? g.Hkv * ((g.nb + 1) / 2) * G : g.Hkv * g.nb * (G / 2)));
+#define RR_PP_LAUNCH(DV, ODD)                                                                      \
+  attn_bf16_pp_kernel<DV, 128, ODD><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
+                                                           g.nb, g.causal, cscale, g.L)
         if (g.d == 128) {
           if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
         } else {
           if (G % 2) RR_PP_LAUNCH(64, true); else RR_PP_LAUNCH(64, false);
         }
 #undef RR_PP_LAUNCH
-        if (G % 2 == 1) {
-          hipError_t e = hipGetLastError();
-          if (e != hipSuccess) return e;
-          const dim3 lgrid((unsigned)(g.Hkv * g.nb));
-          if (g.d == 128)
-            attn_bf16_kernel<128, 128><<<lgrid, 256, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                             g.nb, g.causal, cscale, g.L, G - 1, 1);
-          else
-            attn_bf16_kernel<64, 128><<<lgrid, 256, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                            g.nb, g.causal, cscale, g.L, G - 1, 1);
-        }
         return hipGetLastError();
       }
       if (g.d == 128)

@@ -112,7 +112,8 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  * p->S and p->tau are not used but must be valid.
  * Kernel choice (bf16, B = 128, two or more query heads per KV head): two
  * query heads per workgroup in a ping-pong schedule; with an odd count the
- * last head of every KV head runs in the one-head kernel. The environment
+ * last head of every KV head is paired with itself over two adjacent query
+ * blocks in the same launch. The environment
  * variables RR_ATTN_PP=0 (head pairs without ping-pong) and RR_ATTN_PAIR=0
  * (one head per workgroup), read at every call, select the other kernels for
  * measurement; results agree with the default within bf16 rounding.

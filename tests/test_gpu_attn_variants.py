@@ -9,10 +9,12 @@ the three outputs with each other within 1e-2 (the two head-pair kernels sum
 the same products in the same order; the one-head kernel forms the row sums
 from the unrounded probabilities).
 
-Shapes: an odd group (by default its last head runs in the one-head kernel
-next to the ping-pong pairs; the head-pair kernel leaves half a workgroup idle),
-a non-causal problem with a short last block, head dimension 64, and lists
-that the search produced, so heads of one pair select different blocks.
+Shapes: odd groups (by default the last head of each KV head runs paired with
+itself over two adjacent query blocks, one per slot; with an odd number of
+query blocks the lowest block's lone head has no partner; the head-pair kernel
+leaves half a workgroup idle instead), causal and not, a non-causal problem with
+a short last block, head dimension 64, and lists that the search produced, so
+heads of one pair select different blocks.
 """
 
 import os
@@ -37,6 +39,8 @@ def g(name, L, Hq, Hkv, d, S, causal=True, kind="llm", seed=300):
 
 CASES = [
     g("odd_group_g3", 1536, 6, 2, 128, 16),
+    g("odd_group_g3_odd_nb", 1400, 3, 1, 128, 8),
+    g("odd_group_g5_noncausal_d64", 1100, 10, 2, 64, 16, causal=False, kind="gauss"),
     g("noncausal_short_tail", 1000, 4, 2, 128, 16, causal=False, kind="gauss"),
     g("d64_g4", 1024, 8, 2, 64, 16),
 ]
