@@ -582,8 +582,15 @@ __device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8
   __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
 }
 
+// Rows (of n) after which the KV head an XCD serves moves on by one: each XCD
+// then serves every KV head over the launch, so KV heads whose rows select
+// more blocks do not keep one XCD busy after the others, while the rows in
+// flight on an XCD at one time (about 16) mostly share one KV head's tiles.
+__device__ __forceinline__ int rotation_rows(int n) { return n / 16 > 16 ? n / 16 : 16; }
+
 // Launch index -> (KV head g, query block i, head pair p): query blocks in
-// decreasing order, the pairs of one (g, i) on one XCD in consecutive slots.
+// decreasing order, the pairs of one (g, i) on one XCD in consecutive slots;
+// for each query block the KV heads rotate over the XCDs (rotation_rows).
 __device__ __forceinline__ void pair_item(int x, int Hkv, int nb, int npairs, int& g, int& i, int& p) {
   const int nunits = Hkv * nb;
   int u;
@@ -595,8 +602,9 @@ __device__ __forceinline__ void pair_item(int x, int Hkv, int nb, int npairs, in
     u = x / npairs;
     p = x % npairs;
   }
-  i = nb - 1 - u / Hkv;
-  g = u % Hkv;
+  const int r = u / Hkv;  // rows longest first
+  i = nb - 1 - r;
+  g = (u % Hkv + r / rotation_rows(nb)) % Hkv;
 }
 
 // Work item x of the ping-pong kernel for an odd group size G: unit u = (KV
@@ -617,7 +625,7 @@ __device__ __forceinline__ void odd_item(int x, int Hkv, int npb, int G, int& g,
     it = x % G;
   }
   pb = u / Hkv;
-  g = u % Hkv;
+  g = (u % Hkv + pb / rotation_rows(npb)) % Hkv;
 }
 
 template <int D, int BLK>
