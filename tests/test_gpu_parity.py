@@ -145,9 +145,14 @@ def _workload_case(name, tau, full_search, n_rows_sample=192, search_rows=None):
     res = check_lists(w, tau, rc, ci, orc, rows=rows)
     keep = rc.sum() / (w.Hq * w.nb * (w.nb + 1) / 2)
     say(f"  keep fraction {keep:.4f}")
-    # attention on the GPU's lists, compared on sampled rows (full for tiny)
+    # attention on the GPU's lists, compared on sampled rows (full for tiny);
+    # the output starts as NaN, so a (head, query block) the attention's work
+    # schedule never ran shows up at any size
+    run.pre.out.fill_(float("nan"))
     out, rc2, ci2 = run.prefill()
     np.testing.assert_array_equal(rc2, rc)
+    assert np.isfinite(out).all(), "some output rows were never written"
+
     tmax, tmean = tol(w)
     if w.L <= 1024:
         want = oracle.attention(run.q, run.k, run.v, rc2, ci2, B=w.B, causal=w.causal)
