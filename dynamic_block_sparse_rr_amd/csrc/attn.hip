@@ -76,9 +76,11 @@ __host__ __device__ __forceinline__ int key_of_pos(int p) {
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
-                                                          __bf16* __restrict__ vt, int Hkv, int nb, int L) {
+                                                          __bf16* __restrict__ vt, int Hkv, int nb, int L,
+                                                          int32_t* __restrict__ queues) {
   // one workgroup per (g, key block j); tile BLK keys x D channels
   __shared__ uint16_t tile[BLK][D + 2];
+  if (blockIdx.x == 0 && threadIdx.x < kAttnQueues) queues[threadIdx.x] = 0;  // the attention's work queues
   const int j = blockIdx.x % nb;
   const int g = blockIdx.x / nb;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(v);
@@ -887,11 +889,47 @@ __device__ __forceinline__ void pp_pv(const PairCtx<D, BLK>& cx, const uint8_t* 
 // ODD: the group size is odd and work items are decoded by odd_item (each
 // slot then has its own query block); otherwise by pair_item (both slots on
 // one query block).
+// Work queues of the ping-pong kernel: the nitems items split into nq
+// interleaved queues (item x in queue x mod nq; with nq = kAttnQueues this is
+// the split of pair_item and odd_item over the XCDs). A workgroup claims the
+// next unclaimed item of its own XCD's queue or, once that is empty, of the
+// following queues. Returns -1 when every queue is empty. Called by all
+// threads of the workgroup (one barrier).
+static_assert(kAttnQueues == 8, "pair_item and odd_item spread items over the 8 XCDs");
+__device__ __forceinline__ int claim_item(int32_t* queues, int nq, int nitems) {
+  __shared__ int claimed;
+  if (threadIdx.x == 0) {
+    const int per = nitems / nq;
+    const int own = blockIdx.x % nq;
+    int got = -1;
+    for (int s = 0; s < nq && got < 0; ++s) {
+      const int qi = (own + s) % nq;
+      const int t = __hip_atomic_fetch_add(queues + qi, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < per) got = t * nq + qi;
+    }
+    claimed = got;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(claimed);
+}
+
+// ODD: the group size is odd and work items are decoded by odd_item (each
+// slot then has its own query block); otherwise by pair_item (both slots on
+// one query block). two == 0: workgroup x runs item x. two == 1: as many
+// workgroups as items, each claiming up to two items from the work queues
+// (claim_item; counters zero at launch, nitems a multiple of nq). The
+// workgroups of an XCD that runs faster then drain its queue two items at a
+// time and go on to the other XCDs' items, so the XCDs finish together; each
+// counter increment hands out at most one item, so every item runs exactly
+// once, and workgroups that find every queue empty exit at once. The two
+// items are two straight-line copies of the body: a loop over items makes the
+// compiler keep its whole register budget and spill.
 template <int D, int BLK, bool ODD>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pp_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
     const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
+    int Hq, int Hkv, int nb, int causal, float cscale, int L, int32_t* __restrict__ queues, int nq, int nitems,
+    int two) {
   typedef PairCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   constexpr int MT = C::MT;
@@ -900,209 +938,221 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[C::TILE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  C cx;
-  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int slot = cx.wave / C::WPH;  // 0: head A (MFMAs in even half-steps), 1: head B
-  const int n32 = lane & 31;
-  cx.half = lane >> 5;
-  cx.qr = (cx.wave % C::WPH) * 32 + n32;
-  cx.cscale = cscale;
-  const int G = Hq / Hkv;
-  // slot 0 runs head hA on query block iA, slot 1 head hB on block iB
-  int g, hA, hB, iA, iB;
-  bool hasB = true;
-  if constexpr (!ODD) {  // G even: heads 2p and 2p+1 of one query block
-    int p;
-    pair_item(blockIdx.x, Hkv, nb, G / 2, g, iA, p);
-    iB = iA;
-    hA = g * G + 2 * p;
-    hB = hA + 1;
-  } else {
-    int pb, it;
-    odd_item(blockIdx.x, Hkv, (nb + 1) / 2, G, g, pb, it);
-    const int i0 = nb - 1 - 2 * pb, i1 = i0 - 1;
-    if (it < 2 * (G / 2)) {
-      iA = iB = it < G / 2 ? i0 : i1;
-      if (iA < 0) return;  // odd nb: the lowest unit has one block (uniform exit, before any barrier)
-      hA = g * G + 2 * (it % (G / 2));
+  // one work item; returns early (per thread) where the item or a row ends
+  auto process = [&](const int item) __attribute__((always_inline)) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    C cx;
+    cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = cx.wave / C::WPH;  // 0: head A (MFMAs in even half-steps), 1: head B
+    const int n32 = lane & 31;
+    cx.half = lane >> 5;
+    cx.qr = (cx.wave % C::WPH) * 32 + n32;
+    cx.cscale = cscale;
+    const int G = Hq / Hkv;
+    // slot 0 runs head hA on query block iA, slot 1 head hB on block iB
+    int g, hA, hB, iA, iB;
+    bool hasB = true;
+    if constexpr (!ODD) {  // G even: heads 2p and 2p+1 of one query block
+      int p;
+      pair_item(item, Hkv, nb, G / 2, g, iA, p);
+      iB = iA;
+      hA = g * G + 2 * p;
       hB = hA + 1;
-    } else {  // the lone head, block i0 in slot 0 and i1 (if any) in slot 1
-      hA = hB = g * G + G - 1;
-      iA = i0;
-      iB = i1;
-      hasB = i1 >= 0;
+    } else {
+      int pb, it;
+      odd_item(item, Hkv, (nb + 1) / 2, G, g, pb, it);
+      const int i0 = nb - 1 - 2 * pb, i1 = i0 - 1;
+      if (it < 2 * (G / 2)) {
+        iA = iB = it < G / 2 ? i0 : i1;
+        if (iA < 0) return;  // odd nb: the lowest unit has one block (uniform exit, before any barrier)
+        hA = g * G + 2 * (it % (G / 2));
+        hB = hA + 1;
+      } else {  // the lone head, block i0 in slot 0 and i1 (if any) in slot 1
+        hA = hB = g * G + G - 1;
+        iA = i0;
+        iB = i1;
+        hasB = i1 >= 0;
+      }
     }
-  }
-  const int h = slot ? hB : hA;
-  const int i = slot ? iB : iA;
-  const bool active = slot == 0 || hasB;
-  const int x = i * BLK + cx.qr;
+    const int h = slot ? hB : hA;
+    const int i = slot ? iB : iA;
+    const bool active = slot == 0 || hasB;
+    const int x = i * BLK + cx.qr;
 
-  static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
-  {
-    const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
-    cx.koff = (kr * Hkv * D + kc * 8) * 2;
-    cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
-    cx.voff = tid * 16;  // Vt tiles are copied as stored
-    cx.vstep = C::NTHR * 16;
-  }
-  cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
-  cx.vro = (cx.half * D + n32) * 16;
-  cx.vro_hi = cx.vro + C::VBIAS;  // see attn_bf16_pair_kernel
-  asm volatile("" : "+v"(cx.vro_hi));
+    static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
+    {
+      const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
+      cx.koff = (kr * Hkv * D + kc * 8) * 2;
+      cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
+      cx.voff = tid * 16;  // Vt tiles are copied as stored
+      cx.vstep = C::NTHR * 16;
+    }
+    cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
+    cx.vro = (cx.half * D + n32) * 16;
+    cx.vro_hi = cx.vro + C::VBIAS;  // see attn_bf16_pair_kernel
+    asm volatile("" : "+v"(cx.vro_hi));
 
-  bf16x8 qf[C::DK];
-  if (active && x < L) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
+    bf16x8 qf[C::DK];
+    if (active && x < L) {
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
 #pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
-  } else {
+      for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
+    } else {
 #pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
-  }
+      for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
+    }
 
-  // the two block lists, merged on the fly (all values wave-uniform)
-  const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
-  // largest admissible key block of each slot's row, and of the merged walk (iA >= iB)
-  const int jlastA = causal ? iA : nb - 1;
-  const int jlastB = causal ? iB : nb - 1;
-  const int jlast = jlastA;
-  // each slot's masked block, if any: its causal diagonal, else a short last block
-  const int jdiagA = causal ? iA : (ltail < BLK ? nb - 1 : nb);
-  const int jdiagB = causal ? iB : (ltail < BLK ? nb - 1 : nb);
-  const int klim = causal ? cx.qr : ltail - 1;
-  const size_t rowA = (size_t)hA * nb + iA, rowB = (size_t)hB * nb + iB;
-  const int cntA = min(max(row_count[rowA], 0), nb);
-  const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
-  const int32_t* la = col_idx + rowA * nb;
-  const int32_t* lb = col_idx + rowB * nb;
-  constexpr int kNone = 1 << 30;
-  int ia = 0, ib = 0;
-  int ja = cntA > 0 ? min(max(la[0], 0), jlastA) : kNone;
-  int jb = cntB > 0 ? min(max(lb[0], 0), jlastB) : kNone;
+    // the two block lists, merged on the fly (all values wave-uniform)
+    const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
+    // largest admissible key block of each slot's row, and of the merged walk (iA >= iB)
+    const int jlastA = causal ? iA : nb - 1;
+    const int jlastB = causal ? iB : nb - 1;
+    const int jlast = jlastA;
+    // each slot's masked block, if any: its causal diagonal, else a short last block
+    const int jdiagA = causal ? iA : (ltail < BLK ? nb - 1 : nb);
+    const int jdiagB = causal ? iB : (ltail < BLK ? nb - 1 : nb);
+    const int klim = causal ? cx.qr : ltail - 1;
+    const size_t rowA = (size_t)hA * nb + iA, rowB = (size_t)hB * nb + iB;
+    const int cntA = min(max(row_count[rowA], 0), nb);
+    const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
+    const int32_t* la = col_idx + rowA * nb;
+    const int32_t* lb = col_idx + rowB * nb;
+    constexpr int kNone = 1 << 30;
+    int ia = 0, ib = 0;
+    int ja = cntA > 0 ? min(max(la[0], 0), jlastA) : kNone;
+    int jb = cntB > 0 ? min(max(lb[0], 0), jlastB) : kNone;
 
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
-  const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
-  const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
+    const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
 
-  f32x16 oacc[C::NT];
+    f32x16 oacc[C::NT];
 #pragma unroll
-  for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
-  float mrow = -INFINITY, lrow = 0.0f;
-  f32x16 sacc[MT];
-  bf16x8 pf[MT][2];
+    for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
+    float mrow = -INFINITY, lrow = 0.0f;
+    f32x16 sacc[MT];
+    bf16x8 pf[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
+    for (int mt = 0; mt < MT; ++mt) sacc[mt] = f32x16{};
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) pf[mt][0] = pf[mt][1] = bf16x8{};
+    for (int mt = 0; mt < MT; ++mt) pf[mt][0] = pf[mt][1] = bf16x8{};
 
-  constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
-  const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
-  const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
-  auto copy_k = [&](int jj, uint8_t* dst) {
-    const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jj * kstride, k_bytes, kbytes);
-    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jj * kstride, kb), cx.koff, cx.kstep, dst);
-  };
-  auto copy_v = [&](int jj, uint8_t* dst) {
-    pair_copy<D, BLK, 1>(cx, tile_rsrc(vg + (size_t)jj * C::TILE, C::TILE), cx.voff, cx.vstep, dst);
-  };
-  int j = min(ja, jb);  // block n of the merged list (> jlast: the list is done)
-  if (j <= jlast) copy_k(j, lds_k0);
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
-  __builtin_amdgcn_s_barrier();
+    constexpr int kWaitAll = 0x0070;  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
+    const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
+    auto copy_k = [&](int jj, uint8_t* dst) {
+      const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jj * kstride, k_bytes, kbytes);
+      pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jj * kstride, kb), cx.koff, cx.kstep, dst);
+    };
+    auto copy_v = [&](int jj, uint8_t* dst) {
+      pair_copy<D, BLK, 1>(cx, tile_rsrc(vg + (size_t)jj * C::TILE, C::TILE), cx.voff, cx.vstep, dst);
+    };
+    int j = min(ja, jb);  // block n of the merged list (> jlast: the list is done)
+    if (j <= jlast) copy_k(j, lds_k0);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
 
-  // Block n with K(n) in kc and V(n-1) in vp; K(n+1) is copied to kn and V(n)
-  // to vc. Returns false after the step past the last block (which only
-  // finishes the last P V). SLOT is this wave's head: 0 issues its MFMAs in
-  // the first half-step, 1 in the second.
-  auto run = [&](auto slot_c) __attribute__((always_inline)) {
-    constexpr int SLOT = decltype(slot_c)::value;
-    bool sel_prev = false;  // this wave's head selected block n-1
-    auto mfma_phase = [&](bool sel, bool diag, const uint8_t* kc, const uint8_t* vp) __attribute__((always_inline)) {
-      if (sel_prev) pp_pv<D, BLK>(cx, vp, pf, oacc);
-      if (sel) {
-        pp_qk<D, BLK>(cx, kc, qf, sacc);
-        if (diag) {  // keys past the lane's limit get score -inf (probability zero)
+    // Block n with K(n) in kc and V(n-1) in vp; K(n+1) is copied to kn and V(n)
+    // to vc. Returns false after the step past the last block (which only
+    // finishes the last P V). SLOT is this wave's head: 0 issues its MFMAs in
+    // the first half-step, 1 in the second.
+    auto run = [&](auto slot_c) __attribute__((always_inline)) {
+      constexpr int SLOT = decltype(slot_c)::value;
+      bool sel_prev = false;  // this wave's head selected block n-1
+      auto mfma_phase = [&](bool sel, bool diag, const uint8_t* kc, const uint8_t* vp) __attribute__((always_inline)) {
+        if (sel_prev) pp_pv<D, BLK>(cx, vp, pf, oacc);
+        if (sel) {
+          pp_qk<D, BLK>(cx, kc, qf, sacc);
+          if (diag) {  // keys past the lane's limit get score -inf (probability zero)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
-              if (key > klim) sacc[mt][v] = -INFINITY;
-            }
+              for (int v = 0; v < 16; ++v) {
+                const int key = mt * 32 + 8 * (v >> 2) + 4 * cx.half + (v & 3);
+                if (key > klim) sacc[mt][v] = -INFINITY;
+              }
+          }
         }
-      }
-    };
-    auto step = [&](const uint8_t* kc, uint8_t* kn, const uint8_t* vp, uint8_t* vc) __attribute__((always_inline)) {
-      const bool have = j <= jlast;
-      const bool selA = have && ja == j, selB = have && jb == j;
-      if (selA) {
-        ++ia;
-        ja = ia < cntA ? min(max(la[ia], 0), jlastA) : kNone;
-      }
-      if (selB) {
-        ++ib;
-        jb = ib < cntB ? min(max(lb[ib], 0), jlastB) : kNone;
-      }
-      const int jn = min(ja, jb);
-      const bool sel = SLOT ? selB : selA;
-      const bool diag = have && j == (SLOT ? jdiagB : jdiagA);
-      // each wave issues its share of the copies of K(n+1) and V(n) in
-      // half-step 2n where it is off the critical path: head B before its
-      // softmax, head A after its MFMAs
-      auto copies = [&]() __attribute__((always_inline)) {
-        if (jn <= jlast) copy_k(jn, kn);
-        if (have) copy_v(j, vc);
       };
-      // half-step 2n
-      if (SLOT == 0) {
-        mfma_phase(sel, diag, kc, vp);
-        copies();
-      } else {
-        copies();
-        if (sel_prev) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+      auto step = [&](const uint8_t* kc, uint8_t* kn, const uint8_t* vp, uint8_t* vc) __attribute__((always_inline)) {
+        const bool have = j <= jlast;
+        const bool selA = have && ja == j, selB = have && jb == j;
+        if (selA) {
+          ++ia;
+          ja = ia < cntA ? min(max(la[ia], 0), jlastA) : kNone;
+        }
+        if (selB) {
+          ++ib;
+          jb = ib < cntB ? min(max(lb[ib], 0), jlastB) : kNone;
+        }
+        const int jn = min(ja, jb);
+        const bool sel = SLOT ? selB : selA;
+        const bool diag = have && j == (SLOT ? jdiagB : jdiagA);
+        // each wave issues its share of the copies of K(n+1) and V(n) in
+        // half-step 2n where it is off the critical path: head B before its
+        // softmax, head A after its MFMAs
+        auto copies = [&]() __attribute__((always_inline)) {
+          if (jn <= jlast) copy_k(jn, kn);
+          if (have) copy_v(j, vc);
+        };
+        // half-step 2n
+        if (SLOT == 0) {
+          mfma_phase(sel, diag, kc, vp);
+          copies();
+        } else {
+          copies();
+          if (sel_prev) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+        }
+        __builtin_amdgcn_s_barrier();
+        // half-step 2n+1
+        if (SLOT == 0) {
+          if (sel) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
+        } else {
+          mfma_phase(sel, diag, kc, vp);
+        }
+        // this block's reads are done and the copies issued at its start have landed
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __builtin_amdgcn_s_barrier();
+        sel_prev = sel;
+        j = jn;
+        return have;
+      };
+      // two blocks per trip, so that each stage's LDS objects are known at compile time
+      while (step(lds_k0, lds_k1, lds_v1, lds_v0) && step(lds_k1, lds_k0, lds_v0, lds_v1)) {
       }
-      __builtin_amdgcn_s_barrier();
-      // half-step 2n+1
-      if (SLOT == 0) {
-        if (sel) pair_softmax<D, BLK, false>(cx, sacc, oacc, mrow, lrow, pf, 0);
-      } else {
-        mfma_phase(sel, diag, kc, vp);
-      }
-      // this block's reads are done and the copies issued at its start have landed
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      __builtin_amdgcn_s_barrier();
-      sel_prev = sel;
-      j = jn;
-      return have;
     };
-    // two blocks per trip, so that each stage's LDS objects are known at compile time
-    while (step(lds_k0, lds_k1, lds_v1, lds_v0) && step(lds_k1, lds_k0, lds_v0, lds_v1)) {
+    if (slot == 0)
+      run(IntConst<0>{});
+    else
+      run(IntConst<1>{});
+
+    if (!active || x >= L) return;
+    const float ltot = lrow + __shfl_xor(lrow, 32);
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const int e = t * 32 + 8 * v4 + 4 * cx.half;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(dst + e) = w;
+      }
     }
   };
-  if (slot == 0)
-    run(IntConst<0>{});
-  else
-    run(IntConst<1>{});
 
-  if (!active || x >= L) return;
-  const float ltot = lrow + __shfl_xor(lrow, 32);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int e = t * 32 + 8 * v4 + 4 * cx.half;
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
-      w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(dst + e) = w;
-    }
-  }
+  const int item0 = two ? claim_item(queues, nq, nitems) : (int)blockIdx.x;
+  if (item0 < 0) return;  // uniform
+  process(item0);
+  if (!two) return;
+  __syncthreads();  // this item's LDS reads and the claimed index are done
+  const int item1 = claim_item(queues, nq, nitems);
+  if (item1 < 0) return;
+  process(item1);
 }
 
 // Variant switch: RR_ATTN_PP=0 selects the head-pair kernel without ping-pong
@@ -1183,20 +1233,20 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStream_t st) {
+hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_t* queues, hipStream_t st) {
   const dim3 grid((unsigned)(g.Hkv * g.nb));
   const __bf16* vv = static_cast<const __bf16*>(v);
   __bf16* out = static_cast<__bf16*>(vt);
-  if (g.d == 128 && g.B == 128) transpose_v_kernel<128, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
-  else if (g.d == 128 && g.B == 64) transpose_v_kernel<128, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
-  else if (g.d == 64 && g.B == 128) transpose_v_kernel<64, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
-  else transpose_v_kernel<64, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L);
+  if (g.d == 128 && g.B == 128) transpose_v_kernel<128, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
+  else if (g.d == 128 && g.B == 64) transpose_v_kernel<128, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
+  else if (g.d == 64 && g.B == 128) transpose_v_kernel<64, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
+  else transpose_v_kernel<64, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
-                            const void* vt, const int32_t* row_count, const int32_t* col_idx,
-                            void* out, hipStream_t st) {
+                            const void* vt, int32_t* queues, const int32_t* row_count,
+                            const int32_t* col_idx, void* out, hipStream_t st) {
   const float cscale = (1.0f / sqrtf((float)g.d)) * 1.4426950408889634f;
   const dim3 grid((unsigned)(g.Hq * g.nb));
   if (g.bf16) {
@@ -1218,10 +1268,21 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
         // Even group: G/2 head pairs per (KV head, query block). Odd group: G
         // items per (KV head, two query blocks), the lone head of the group
         // paired with itself over the two blocks (odd_item).
-        const dim3 fgrid((unsigned)(G % 2 ? g.Hkv * ((g.nb + 1) / 2) * G : g.Hkv * g.nb * (G / 2)));
+        const int nunits = G % 2 ? g.Hkv * ((g.nb + 1) / 2) : g.Hkv * g.nb;
+        const int nitems = G % 2 ? nunits * G : nunits * (G / 2);
+        // Two items per workgroup from per-XCD queues where the items map onto
+        // the XCDs and each CU has many of them; below that the claims' atomic
+        // round trips cost more than the balance gains.
+        const int nq = nunits % kAttnQueues == 0 ? kAttnQueues : 1;
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int two = nq == kAttnQueues && ncu > 0 && nitems > 16 * ncu ? 1 : 0;
+        const dim3 fgrid((unsigned)nitems);
 #define RR_PP_LAUNCH(DV, ODD)                                                                      \
   attn_bf16_pp_kernel<DV, 128, ODD><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
-                                                           g.nb, g.causal, cscale, g.L)
+                                                           g.nb, g.causal, cscale, g.L, queues, nq, nitems, two)
         if (g.d == 128) {
           if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
         } else {

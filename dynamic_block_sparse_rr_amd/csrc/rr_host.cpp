@@ -52,7 +52,7 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
 }
 
 struct Workspace {
-  size_t kbar, mass, vt, total;  // byte offsets and total size
+  size_t kbar, mass, vt, queues, total;  // byte offsets and total size
 };
 
 Workspace layout(const rr::Geometry& g) {
@@ -65,6 +65,8 @@ Workspace layout(const rr::Geometry& g) {
   off += align_up((size_t)g.Hq * g.nb * g.nb * sizeof(float));
   w.vt = off;  // nb whole tiles: a short last block is padded with zeros
   if (g.bf16) off += align_up((size_t)g.nb * g.B * g.Hkv * g.d * esz);
+  w.queues = off;  // the attention's work-queue counters
+  if (g.bf16) off += align_up(rr::kAttnQueues * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -93,9 +95,10 @@ rr_status run_attention(const rr::Geometry& g, const void* q, const void* k, con
                         hipStream_t st) {
   const Workspace w = layout(g);
   void* vt = static_cast<uint8_t*>(ws) + w.vt;
+  int32_t* queues = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + w.queues);
   hipError_t e = hipSuccess;
-  if (g.bf16) e = rr::launch_transpose_v(g, v, vt, st);
-  if (e == hipSuccess) e = rr::launch_attention(g, q, k, v, vt, row_count, col_idx, out, st);
+  if (g.bf16) e = rr::launch_transpose_v(g, v, vt, queues, st);
+  if (e == hipSuccess) e = rr::launch_attention(g, q, k, v, vt, queues, row_count, col_idx, out, st);
   return hip_status(e);
 }
 

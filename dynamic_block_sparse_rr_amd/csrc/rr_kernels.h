@@ -31,11 +31,14 @@ hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, in
 hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,
                               int32_t* out_count, int32_t* out_idx, hipStream_t st);
 
-// Stage 2 launches.
-hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, hipStream_t st);
+// Stage 2 launches. queues: kAttnQueues device counters of the bf16
+// attention's work queues (one per XCD); launch_transpose_v zeroes them, so
+// the two run in this order on one stream, one pair per call at a time.
+constexpr int kAttnQueues = 8;
+hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_t* queues, hipStream_t st);
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
-                            const void* vt, const int32_t* row_count, const int32_t* col_idx,
-                            void* out, hipStream_t st);
+                            const void* vt, int32_t* queues, const int32_t* row_count,
+                            const int32_t* col_idx, void* out, hipStream_t st);
 
 // Selection quality: full-attention softmax mass inside the selected blocks.
 hipError_t launch_recall(const Geometry& g, const void* q, const void* k, const int32_t* row_count,

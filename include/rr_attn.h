@@ -107,7 +107,9 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  * give undefined output (the library does not read lists back to the host).
  *   q, k, v     device inputs in p->dtype; out: device output [L][Hq][d] in p->dtype.
  *   ws          device workspace (bf16: holds a copy of V re-laid out as one
- *               channels-by-keys tile per key block).
+ *               channels-by-keys tile per key block, and the counters of the
+ *               attention's work queues; calls that overlap in time need
+ *               workspaces of their own).
  * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
  * p->S and p->tau are not used but must be valid.
  * Kernel choice (bf16, B = 128, two or more query heads per KV head): two

@@ -49,13 +49,13 @@ def test_workspace_bytes():
     p = base()
     n = rr.rr_workspace_bytes(p)
     ns, nb = 16384 // 16, 16384 // 128
-    # pooled keys + block masses + key-major V copy, each 256-byte aligned
-    assert n == ns * 8 * 128 * 2 + 32 * nb * nb * 4 + 16384 * 8 * 128 * 2
+    # pooled keys + block masses + key-major V copy + work-queue counters, each 256-byte aligned
+    assert n == ns * 8 * 128 * 2 + 32 * nb * nb * 4 + 16384 * 8 * 128 * 2 + 256
     assert rr.rr_workspace_bytes(base(dtype=rr.RR_FP32)) == ns * 8 * 128 * 4 + 32 * nb * nb * 4
     # a ragged length: ceil(L / B) blocks, ceil(L / S) strides, V copy padded to whole blocks
     n = rr.rr_workspace_bytes(base(L=1000))
     al = lambda x: -(-x // 256) * 256
-    assert n == al(63 * 8 * 128 * 2) + al(32 * 8 * 8 * 4) + al(8 * 128 * 8 * 128 * 2)
+    assert n == al(63 * 8 * 128 * 2) + al(32 * 8 * 8 * 4) + al(8 * 128 * 8 * 128 * 2) + 256
 
 
 @pytest.mark.parametrize("kw,status", [
