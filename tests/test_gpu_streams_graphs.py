@@ -59,10 +59,14 @@ def test_two_streams_at_once_match_sequential_calls():
     say("  two streams: both results bitwise equal to sequential calls")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (6, 2)], ids=["group4", "group3_two_launches"])
-def test_prefill_graph_replays_match_eager_calls(hq, hkv):
-    # an odd group makes the attention two launches (head pairs, then the last heads)
-    w = Workload("g", 4096, hq, hkv, 128, "bf16", 128, 16, (0.9,), 33, "llm", 8)
+@pytest.mark.parametrize("L,hq,hkv", [(4096, 8, 2), (4096, 6, 2), (40960, 32, 8)],
+                         ids=["group4", "group3_odd", "claimed_items"])
+def test_prefill_graph_replays_match_eager_calls(L, hq, hkv):
+    # group3_odd: the lone head of each group runs paired with itself over two query
+    # blocks; claimed_items: 5,120 head-pair items, enough per CU on a 256-CU GPU that
+    # the attention's workgroups claim up to two items each from the per-XCD queues
+    # (counters zeroed inside the captured work at every replay)
+    w = Workload("g", L, hq, hkv, 128, "bf16", 128, 16, (0.9,), 33, "llm", 8)
     job = Job(w)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -76,7 +80,7 @@ def test_prefill_graph_replays_match_eager_calls(hq, hkv):
     torch.cuda.synchronize()
     for rep in range(3):
         # new inputs in the captured buffers, then the replay, then the eager call on the same inputs
-        q, k, v = make_inputs(Workload("g", 4096, hq, hkv, 128, "bf16", 128, 16, (0.9,), 40 + rep, "llm", 8))
+        q, k, v = make_inputs(Workload("g", L, hq, hkv, 128, "bf16", 128, 16, (0.9,), 40 + rep, "llm", 8))
         job.q.copy_(q.cuda())
         job.k.copy_(k.cuda())
         job.v.copy_(v.cuda())
