@@ -87,7 +87,7 @@ def search_logits(w, rows=None) -> int:
 def cpu_baseline(w, q, k, v, rc, ci, f_comp, seconds_hint=20.0):
     """The oracle timed on a bounded sample, extrapolated to the whole step."""
     import oracle
-    from tests.gpu_cases import sample_rows
+    from synthetic.rows import sample_rows
 
     cores = oracle.max_threads()
     rows_i = sorted({w.nb // 4, w.nb // 2, (3 * w.nb) // 4})

@@ -122,11 +122,46 @@ def _ptr(x):
 
 
 def _nbytes(ws, ws_bytes):
-    if ws_bytes is not None:
-        return int(ws_bytes)
     if hasattr(ws, "numel"):
-        return ws.numel() * ws.element_size()
-    return 0
+        have = ws.numel() * ws.element_size()
+        if ws_bytes is not None and int(ws_bytes) > have:
+            raise ValueError("ws_bytes (%d) exceeds the workspace tensor (%d bytes)" % (int(ws_bytes), have))
+        return have if ws_bytes is None else int(ws_bytes)
+    return 0 if ws_bytes is None else int(ws_bytes)
+
+
+def _dt(p):
+    """torch dtype of the problem's tensors."""
+    import torch
+
+    return torch.bfloat16 if p.dtype == RR_BF16 else torch.float32
+
+
+def _want(x, name, dtype, numel):
+    """Check a tensor argument against what the problem needs before its
+    address reaches the library (which cannot check sizes or types); ints
+    (raw device addresses) and None pass through unchecked."""
+    if x is None or isinstance(x, int) or not hasattr(x, "dtype"):
+        return
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError("%s: expected dtype %s, got %s" % (name, dtype, x.dtype))
+    if x.numel() < numel:
+        raise ValueError("%s: expected at least %d elements, got %d" % (name, numel, x.numel()))
+
+
+def _check_qkv(p, q=None, k=None, v=None, out=None):
+    dt = _dt(p)
+    _want(q, "q", dt, p.L * p.Hq * p.d)
+    _want(k, "k", dt, p.L * p.Hkv * p.d)
+    _want(v, "v", dt, p.L * p.Hkv * p.d)
+    _want(out, "out", dt, p.L * p.Hq * p.d)
+
+
+def _check_lists(p, row_count, col_idx, prefix=""):
+    import torch
+
+    _want(row_count, prefix + "row_count", torch.int32, p.Hq * p.nb)
+    _want(col_idx, prefix + "col_idx", torch.int32, p.Hq * p.nb * p.nb)
 
 
 def _stream(stream):
@@ -149,29 +184,48 @@ def rr_workspace_bytes(p: Problem) -> int:
 
 
 def rr_pattern_search(p, q, k, row_count, col_idx, block_mass, ws, ws_bytes=None, stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    import torch
+
+    _check_qkv(p, q, k)
+    _check_lists(p, row_count, col_idx)
+    _want(block_mass, "block_mass", torch.float32, p.Hq * p.nb * p.nb)
     _check("rr_pattern_search", load().rr_pattern_search(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx), _ptr(block_mass),
-        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(ws), nws, _stream(stream)))
 
 
 def rr_block_sparse_attn(p, q, k, v, row_count, col_idx, out, ws, ws_bytes=None, stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    _check_qkv(p, q, k, v, out)
+    _check_lists(p, row_count, col_idx)
     _check("rr_block_sparse_attn", load().rr_block_sparse_attn(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_count), _ptr(col_idx), _ptr(out),
-        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(ws), nws, _stream(stream)))
 
 
 def rr_prefill(p, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    _check_qkv(p, q, k, v, out)
+    _check_lists(p, row_count, col_idx)
     _check("rr_prefill", load().rr_prefill(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
-        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(ws), nws, _stream(stream)))
 
 
 def rr_mass_recall(p, q, k, row_count, col_idx, recall, stream=None):
+    import torch
+
+    _check_qkv(p, q, k)
+    _check_lists(p, row_count, col_idx)
+    _want(recall, "recall", torch.float32, p.Hq * p.nb)
     _check("rr_mass_recall", load().rr_mass_recall(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(row_count), _ptr(col_idx), _ptr(recall), _stream(stream)))
 
 
 def rr_share_group_lists(p, row_count, col_idx, shared_row_count, shared_col_idx, stream=None):
+    _check_lists(p, row_count, col_idx)
+    _check_lists(p, shared_row_count, shared_col_idx, "shared_")
     _check("rr_share_group_lists", load().rr_share_group_lists(
         ctypes.byref(p), _ptr(row_count), _ptr(col_idx), _ptr(shared_row_count), _ptr(shared_col_idx),
         _stream(stream)))
@@ -179,9 +233,16 @@ def rr_share_group_lists(p, row_count, col_idx, shared_row_count, shared_col_idx
 
 def rr_pattern_search_heads(p, q, k, tau_per_head, row_count, col_idx, block_mass, ws, ws_bytes=None,
                             stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    import torch
+
+    _check_qkv(p, q, k)
+    _check_lists(p, row_count, col_idx)
+    _want(tau_per_head, "tau_per_head", torch.float32, p.Hq)
+    _want(block_mass, "block_mass", torch.float32, p.Hq * p.nb * p.nb)
     _check("rr_pattern_search_heads", load().rr_pattern_search_heads(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(tau_per_head), _ptr(row_count), _ptr(col_idx), _ptr(block_mass),
-        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(ws), nws, _stream(stream)))
 
 
 def _lens(seq_lens):
@@ -197,29 +258,57 @@ def rr_workspace_bytes_varlen(p: Problem, seq_lens) -> int:
 
 
 def rr_prefill_varlen(p, seq_lens, q, k, v, out, row_count, col_idx, ws, ws_bytes=None, stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    import torch
+
     a, ptr = _lens(seq_lens)
+    _check_qkv(p, q, k, v, out)
+    nbs = [-(-int(n) // p.B) for n in a]
+    _want(row_count, "row_count", torch.int32, sum(p.Hq * n for n in nbs))
+    _want(col_idx, "col_idx", torch.int32, sum(p.Hq * n * n for n in nbs))
     _check("rr_prefill_varlen", load().rr_prefill_varlen(
         ctypes.byref(p), int(a.size), ptr, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(row_count), _ptr(col_idx),
-        _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(ws), nws, _stream(stream)))
 
 
 def rr_decode_workspace_bytes(p: Problem) -> int:
     return int(load().rr_decode_workspace_bytes(ctypes.byref(p)))
 
 
+def _check_decode(p, q, k, v, out, row_count, col_idx, block_mass=None, kbar=None):
+    import torch
+
+    dt = _dt(p)
+    _want(q, "q", dt, p.Hq * p.d)
+    _want(k, "k", dt, p.L * p.Hkv * p.d)
+    _want(v, "v", dt, p.L * p.Hkv * p.d)
+    _want(kbar, "kbar", dt, p.ns * p.Hkv * p.d)
+    _want(out, "out", dt, p.Hq * p.d)
+    _want(row_count, "row_count", torch.int32, p.Hq)
+    _want(col_idx, "col_idx", torch.int32, p.Hq * p.nb)
+    _want(block_mass, "block_mass", torch.float32, p.Hq * p.nb)
+
+
 def rr_decode(p, q, k, v, out, row_count, col_idx, block_mass, ws, ws_bytes=None, stream=None, kbar=None):
+    nws = _nbytes(ws, ws_bytes)
+    _check_decode(p, q, k, v, out, row_count, col_idx, block_mass, kbar)
     _check("rr_decode", load().rr_decode(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), _ptr(out), _ptr(row_count), _ptr(col_idx),
-        _ptr(block_mass), _ptr(ws), _nbytes(ws, ws_bytes), _stream(stream)))
+        _ptr(block_mass), _ptr(ws), nws, _stream(stream)))
 
 
 def rr_decode_attend(p, q, k, v, row_count, col_idx, out, ws, ws_bytes=None, stream=None):
+    nws = _nbytes(ws, ws_bytes)
+    _check_decode(p, q, k, v, out, row_count, col_idx)
     _check("rr_decode_attend", load().rr_decode_attend(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(row_count), _ptr(col_idx), _ptr(out), _ptr(ws),
-        _nbytes(ws, ws_bytes), _stream(stream)))
+        nws, _stream(stream)))
 
 
 def rr_pool_keys(p, k, kbar, stream=None):
+    dt = _dt(p)
+    _want(k, "k", dt, p.L * p.Hkv * p.d)
+    _want(kbar, "kbar", dt, p.ns * p.Hkv * p.d)
     _check("rr_pool_keys", load().rr_pool_keys(ctypes.byref(p), _ptr(k), _ptr(kbar), _stream(stream)))
 
 

@@ -28,21 +28,23 @@
 //                first, the G query heads sharing a KV head adjacent and on
 //                the same XCD (dispatch is round-robin over the 8 XCDs), so
 //                K/V tiles are reused from that XCD's L2.
-//   attn_bf16_pair  two query heads of one KV head per workgroup (two waves
-//                per SIMD, one per head), walking the merged block list of
-//                both heads: each K/Vt tile is copied once for both, tiles
-//                double-buffered with one barrier per block.
-//   attn_bf16_pp the default for B = 128 and G >= 2: the head-pair workgroup
-//                in ping-pong, each block split in two half-steps so that one
-//                head's waves issue their MFMAs while the other head's run
-//                the softmax (see the kernel). With an odd group the last
-//                head of each KV head pairs with itself over two adjacent
-//                query blocks (one per slot), so no slot is left idle.
+//   attn_bf16_pp B = 128 and G >= 2: two query heads of one KV head per
+//                workgroup (two waves per SIMD, one per head), walking the
+//                merged block list of both heads, so each K/Vt tile is copied
+//                once for both (double-buffered); each block is split in two
+//                half-steps so that one head's waves issue their MFMAs while
+//                the other head's run the softmax (see the kernel). With an
+//                odd group the last head of each KV head pairs with itself
+//                over two adjacent query blocks (one per slot), so no slot is
+//                left idle. attn_bf16 serves every other bf16 shape (B = 64,
+//                or one query head per KV head).
+// The kernel is chosen from the problem alone (dtype, B, G).
 // float32 path: a plain kernel (one thread per query row, K/V tiles in LDS,
 // online softmax in registers).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
+
+#include <atomic>
 
 #include "rr_kernels.h"
 
@@ -521,69 +523,6 @@ __device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (
   lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
-// One key block for one wave, operands already in LDS (no barriers inside).
-// MASK: keys with index > klim inside the block are masked (the causal
-// diagonal block: the lane's query row; a short last block: its last key).
-template <int D, int BLK, bool MASK>
-__device__ __forceinline__ void pair_tile(const PairCtx<D, BLK>& cx, const uint8_t* lds_k, const uint8_t* lds_v,
-                                          const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32], float& mrow,
-                                          float& lrow, int klim) {
-  typedef PairCtx<D, BLK> C;
-  constexpr int MT = C::MT;
-  constexpr int NT = C::NT;
-  constexpr int DK = C::DK;
-  constexpr int LA = 4;  // operand reads run LA MFMAs ahead through a register ring
-  constexpr int NQK = MT * DK;
-  auto kread = [&](int k) {
-    return *reinterpret_cast<const bf16x8*>(lds_k + (k / DK) * 32 * D * 2 + (cx.kro ^ ((k % DK) << 5)));
-  };
-  f32x16 sacc[MT];
-  bf16x8 ring[LA];
-#pragma unroll
-  for (int k = 0; k < LA; ++k) ring[k] = kread(k);
-#pragma unroll
-  for (int k = 0; k < NQK; ++k) {
-    const bf16x8 a = ring[k % LA];
-    if (k + LA < NQK) ring[k % LA] = kread(k + LA);
-    const int mt = k / DK, cc = k % DK;
-    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], cc ? sacc[mt] : f32x16{}, 0, 0, 0);
-  }
-  // issue order: LA operand reads, then alternately one MFMA and the read LA
-  // steps ahead (left to itself the scheduler keeps only one or two reads in
-  // flight)
-  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);
-#pragma unroll
-  for (int k = 0; k < NQK - LA; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
-  bf16x8 pf[MT][2];
-  pair_softmax<D, BLK, MASK>(cx, sacc, oacc, mrow, lrow, pf, klim);
-  // O^T += Vt P^T
-  constexpr int NPV = NT * MT * 2;
-  auto vread = [&](int k) {
-    const int t = k / (MT * 2), r = k % (MT * 2);
-    return *reinterpret_cast<const bf16x8*>(lds_v + (cx.vro_hi - C::VBIAS) + (2 * r * D + t * 32) * 16);
-  };
-#pragma unroll
-  for (int k = 0; k < LA; ++k) ring[k] = vread(k);
-#pragma unroll
-  for (int k = 0; k < NPV; ++k) {
-    const bf16x8 a = ring[k % LA];
-    if (k + LA < NPV) ring[k % LA] = vread(k + LA);
-    const int t = k / (MT * 2), r = k % (MT * 2);
-    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[r >> 1][r & 1], oacc[t], 0, 0, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, LA, 1);
-#pragma unroll
-  for (int k = 0; k < NPV - LA; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, LA, 1);
-}
-
 // Rows (of n) after which the KV head an XCD serves moves on by one: each XCD
 // then serves every KV head over the launch, so KV heads whose rows select
 // more blocks do not keep one XCD busy after the others, while the rows in
@@ -628,169 +567,6 @@ __device__ __forceinline__ void odd_item(int x, int Hkv, int npb, int G, int& g,
   }
   pb = u / Hkv;
   g = (u % Hkv + pb / rotation_rows(npb)) % Hkv;
-}
-
-template <int D, int BLK>
-__global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pair_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
-    const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale, int L) {
-  typedef PairCtx<D, BLK> C;
-  constexpr int KCH = C::KCH;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_k1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[C::TILE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  C cx;
-  cx.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int slot = cx.wave / C::WPH;  // which head of the pair this wave serves
-  const int n32 = lane & 31;
-  cx.half = lane >> 5;
-  cx.qr = (cx.wave % C::WPH) * 32 + n32;
-  cx.cscale = cscale;
-  const int G = Hq / Hkv;
-  const int npairs = (G + 1) / 2;
-  int g, i, p;
-  pair_item(blockIdx.x, Hkv, nb, npairs, g, i, p);
-  const int hA = g * G + 2 * p;
-  const bool hasB = 2 * p + 1 < G;
-  const int hB = hA + 1;
-  const int h = slot ? hB : hA;
-  const bool active = slot == 0 || hasB;  // a lone last head leaves slot 1 idle
-  const int x = i * BLK + cx.qr;
-
-  static_assert(C::NTHR % KCH == 0, "copy rows must advance evenly");
-  {
-    const int kr = tid / KCH, kc = (tid % KCH) ^ (kr & (KCH - 1));
-    cx.koff = (kr * Hkv * D + kc * 8) * 2;
-    cx.kstep = (C::NTHR / KCH) * Hkv * D * 2;
-    cx.voff = tid * 16;  // Vt tiles are copied as stored
-    cx.vstep = C::NTHR * 16;
-  }
-  cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
-  cx.vro = (cx.half * D + n32) * 16;
-  // The Vt stages follow the two K stages in LDS (at 64 and 96 KiB for d =
-  // 128), beyond the 16-bit offset field of ds_read_b128. Written as lds_v +
-  // vro + offset, every read costs a VALU add (the stage base folds into the
-  // constant, which then does not fit); written as lds_v + (vro_hi - VBIAS) +
-  // offset with vro_hi opaque, the constants cancel against the base and each
-  // read is vro_hi plus an immediate. Either form addresses the same bytes.
-  cx.vro_hi = cx.vro + C::VBIAS;
-  asm volatile("" : "+v"(cx.vro_hi));
-
-  bf16x8 qf[C::DK];
-  if (active && x < L) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)x * Hq + h) * D);
-#pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = src[2 * c + cx.half];
-  } else {
-#pragma unroll
-    for (int c = 0; c < C::DK; ++c) qf[c] = bf16x8{};
-  }
-
-  // the two block lists, merged on the fly (all values wave-uniform)
-  const int ltail = L - (nb - 1) * BLK;   // keys in the last block (BLK unless it is short)
-  const int jlast = causal ? i : nb - 1;  // largest admissible key block
-  // the masked block, if any: the causal diagonal, else a short last block;
-  // either way the last entry of both ascending lists
-  const int jdiag = causal ? i : (ltail < BLK ? nb - 1 : nb);
-  const int klim = causal ? cx.qr : ltail - 1;
-  const size_t rowA = (size_t)hA * nb + i, rowB = (size_t)hB * nb + i;
-  const int cntA = min(max(row_count[rowA], 0), nb);
-  const int cntB = hasB ? min(max(row_count[rowB], 0), nb) : 0;
-  const int32_t* la = col_idx + rowA * nb;
-  const int32_t* lb = col_idx + rowB * nb;
-  constexpr int kNone = 1 << 30;
-  int ia = 0, ib = 0;
-  int ja = cntA > 0 ? min(max(la[0], 0), jlast) : kNone;
-  int jb = cntB > 0 ? min(max(lb[0], 0), jlast) : kNone;
-
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(k) + (size_t)g * D * 2;
-  const uint8_t* vg = reinterpret_cast<const uint8_t*>(vt) + (size_t)g * nb * C::TILE;
-  const size_t kstride = (size_t)BLK * Hkv * D * 2;  // bytes between consecutive key blocks of K
-
-  f32x16 oacc[C::NT];
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
-  float mrow = -INFINITY, lrow = 0.0f;
-
-  // vmcnt(0) lgkmcnt(0) through the builtin, so the compiler's wait
-  // bookkeeping knows the counters are clear
-  constexpr int kWaitAll = 0x0070;
-  __builtin_amdgcn_s_waitcnt(kWaitAll);  // queries are in registers
-  // K rows of block j start at kg + j*kstride (row pitch Hkv*d*2 bytes); its Vt
-  // tile is the contiguous TILE bytes at vg + j*TILE
-  const uint32_t kbytes = (uint32_t)((BLK - 1) * Hkv * D * 2 + D * 2);
-  const size_t k_bytes = (size_t)L * Hkv * D * 2;  // the whole K tensor
-  auto copy_block = [&](int jb_, uint8_t* kdst, uint8_t* vdst) {
-    const uint32_t kb = k_tile_bytes((size_t)g * D * 2 + (size_t)jb_ * kstride, k_bytes, kbytes);
-    pair_copy<D, BLK, KCH>(cx, tile_rsrc(kg + (size_t)jb_ * kstride, kb), cx.koff, cx.kstep, kdst);
-    pair_copy<D, BLK, 1>(cx, tile_rsrc(vg + (size_t)jb_ * C::TILE, C::TILE), cx.voff, cx.vstep, vdst);
-  };
-  int j = min(ja, jb);
-  if (j <= jlast) copy_block(j, lds_k0, lds_v0);
-  // One block j whose tiles are in (kc, vc); the next block's copy goes to
-  // (kn, vn).
-  auto step = [&](const uint8_t* kc, const uint8_t* vc, uint8_t* kn, uint8_t* vn) {
-    const bool selA = ja == j, selB = jb == j;
-    if (selA) {
-      ++ia;
-      ja = ia < cntA ? min(max(la[ia], 0), jlast) : kNone;
-    }
-    if (selB) {
-      ++ib;
-      jb = ib < cntB ? min(max(lb[ib], 0), jlast) : kNone;
-    }
-    const int jn = min(ja, jb);
-    // this block's tiles have landed everywhere, and every wave is done with
-    // the other stage, which the next block's copy now reuses
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    __builtin_amdgcn_s_barrier();
-    if (jn <= jlast) copy_block(jn, kn, vn);
-    if (slot ? selB : selA) pair_tile<D, BLK, false>(cx, kc, vc, qf, oacc, mrow, lrow, BLK - 1);
-    j = jn;
-  };
-  // every block before the diagonal, two per trip so that each stage's LDS
-  // objects are known at compile time; the diagonal, last in both lists, after
-  bool odd = false;
-  while (j < jdiag) {
-    step(lds_k0, lds_v0, lds_k1, lds_v1);
-    if (j >= jdiag) {
-      odd = true;
-      break;
-    }
-    step(lds_k1, lds_v1, lds_k0, lds_v0);
-  }
-  if (j == jdiag) {
-    const bool selA = ja == j, selB = jb == j;
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    __builtin_amdgcn_s_barrier();
-    if (slot ? selB : selA) {
-      if (odd)
-        pair_tile<D, BLK, true>(cx, lds_k1, lds_v1, qf, oacc, mrow, lrow, klim);
-      else
-        pair_tile<D, BLK, true>(cx, lds_k0, lds_v0, qf, oacc, mrow, lrow, klim);
-    }
-  }
-
-  if (!active || x >= L) return;
-  const float ltot = lrow + __shfl_xor(lrow, 32);
-  const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-  uint16_t* dst = reinterpret_cast<uint16_t*>(out) + ((size_t)x * Hq + h) * D;
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-    for (int v4 = 0; v4 < 4; ++v4) {
-      const int e = t * 32 + 8 * v4 + 4 * cx.half;
-      u32x2 w;
-      w[0] = pack_bf16x2(oacc[t][4 * v4] * inv, oacc[t][4 * v4 + 1] * inv);
-      w[1] = pack_bf16x2(oacc[t][4 * v4 + 2] * inv, oacc[t][4 * v4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(dst + e) = w;
-    }
-  }
 }
 
 // ------------------------------------------------------------------ bf16 attention, head pairs in ping-pong
@@ -990,7 +766,14 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     }
     cx.kro = n32 * D * 2 + (((cx.half) ^ (n32 & (KCH - 1))) << 4);
     cx.vro = (cx.half * D + n32) * 16;
-    cx.vro_hi = cx.vro + C::VBIAS;  // see attn_bf16_pair_kernel
+    // The Vt stages follow the two K stages in LDS (at 64 and 96 KiB for d =
+    // 128), beyond the 16-bit offset field of ds_read_b128. Written as lds_v +
+    // vro + offset, every read costs a VALU add (the stage base folds into
+    // the constant, which then does not fit); written as lds_v + (vro_hi -
+    // VBIAS) + offset with vro_hi opaque, the constants cancel against the
+    // base and each read is vro_hi plus an immediate. Either form addresses
+    // the same bytes.
+    cx.vro_hi = cx.vro + C::VBIAS;
     asm volatile("" : "+v"(cx.vro_hi));
 
     bf16x8 qf[C::DK];
@@ -1155,20 +938,6 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   process(item1);
 }
 
-// Variant switch: RR_ATTN_PP=0 selects the head-pair kernel without ping-pong
-// (read at every launch, so that one process can run and test both).
-bool attn_pp_enabled() {
-  const char* e = getenv("RR_ATTN_PP");
-  return !(e && e[0] == '0');
-}
-
-// Variant switch: RR_ATTN_PAIR=0 selects the one-head-per-workgroup kernel
-// (read at every launch, like RR_ATTN_PP).
-bool attn_pair_enabled() {
-  const char* e = getenv("RR_ATTN_PAIR");
-  return !(e && e[0] == '0');
-}
-
 // ------------------------------------------------------------------ fp32 attention
 
 template <int D, int BLK>
@@ -1233,6 +1002,29 @@ __global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__
 
 }  // namespace
 
+// Compute units of the device that runs `st`, looked up once per device (the
+// count never changes while the process runs).
+static hipError_t stream_cu_count(hipStream_t st, int* ncu) {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(st, &dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *ncu = c;
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n <= 0) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  *ncu = n;
+  return hipSuccess;
+}
+
 hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_t* queues, hipStream_t st) {
   const dim3 grid((unsigned)(g.Hkv * g.nb));
   const __bf16* vv = static_cast<const __bf16*>(v);
@@ -1262,41 +1054,30 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
     return hipGetLastError();                                                                     \
   }
     const int G = g.Hq / g.Hkv;
-    if (g.B == 128 && G >= 2 && attn_pair_enabled()) {
-      const dim3 pgrid((unsigned)(g.Hkv * g.nb * ((G + 1) / 2)));
-      if (attn_pp_enabled()) {
-        // Even group: G/2 head pairs per (KV head, query block). Odd group: G
-        // items per (KV head, two query blocks), the lone head of the group
-        // paired with itself over the two blocks (odd_item).
-        const int nunits = G % 2 ? g.Hkv * ((g.nb + 1) / 2) : g.Hkv * g.nb;
-        const int nitems = G % 2 ? nunits * G : nunits * (G / 2);
-        // Two items per workgroup from per-XCD queues where the items map onto
-        // the XCDs and each CU has many of them; below that the claims' atomic
-        // round trips cost more than the balance gains.
-        const int nq = nunits % kAttnQueues == 0 ? kAttnQueues : 1;
-        int dev = 0, ncu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        const int two = nq == kAttnQueues && ncu > 0 && nitems > 16 * ncu ? 1 : 0;
-        const dim3 fgrid((unsigned)nitems);
+    if (g.B == 128 && G >= 2) {
+      // Even group: G/2 head pairs per (KV head, query block). Odd group: G
+      // items per (KV head, two query blocks), the lone head of the group
+      // paired with itself over the two blocks (odd_item).
+      const int nunits = G % 2 ? g.Hkv * ((g.nb + 1) / 2) : g.Hkv * g.nb;
+      const int nitems = G % 2 ? nunits * G : nunits * (G / 2);
+      // Two items per workgroup from per-XCD queues where the items map onto
+      // the XCDs and each CU has more than 16 of them; below that the claims'
+      // atomic round trips cost more than the balance gains.
+      const int nq = nunits % kAttnQueues == 0 ? kAttnQueues : 1;
+      int ncu = 0;
+      const hipError_t e = stream_cu_count(st, &ncu);
+      if (e != hipSuccess) return e;
+      const int two = nq == kAttnQueues && nitems > 16 * ncu ? 1 : 0;
+      const dim3 fgrid((unsigned)nitems);
 #define RR_PP_LAUNCH(DV, ODD)                                                                      \
   attn_bf16_pp_kernel<DV, 128, ODD><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
                                                            g.nb, g.causal, cscale, g.L, queues, nq, nitems, two)
-        if (g.d == 128) {
-          if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
-        } else {
-          if (G % 2) RR_PP_LAUNCH(64, true); else RR_PP_LAUNCH(64, false);
-        }
-#undef RR_PP_LAUNCH
-        return hipGetLastError();
+      if (g.d == 128) {
+        if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
+      } else {
+        if (G % 2) RR_PP_LAUNCH(64, true); else RR_PP_LAUNCH(64, false);
       }
-      if (g.d == 128)
-        attn_bf16_pair_kernel<128, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                              g.nb, g.causal, cscale, g.L);
-      else
-        attn_bf16_pair_kernel<64, 128><<<pgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv,
-                                                             g.nb, g.causal, cscale, g.L);
+#undef RR_PP_LAUNCH
       return hipGetLastError();
     }
     RR_ATTN_CASE(128, 128)

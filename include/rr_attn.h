@@ -112,13 +112,11 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  *               workspaces of their own).
  * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
  * p->S and p->tau are not used but must be valid.
- * Kernel choice (bf16, B = 128, two or more query heads per KV head): two
- * query heads per workgroup in a ping-pong schedule; with an odd count the
- * last head of every KV head is paired with itself over two adjacent query
- * blocks in the same launch. The environment
- * variables RR_ATTN_PP=0 (head pairs without ping-pong) and RR_ATTN_PAIR=0
- * (one head per workgroup), read at every call, select the other kernels for
- * measurement; results agree with the default within bf16 rounding.
+ * The kernel is chosen from the problem alone: bf16 with B = 128 and two or
+ * more query heads per KV head runs two query heads per workgroup in a
+ * ping-pong schedule (with an odd count the last head of every KV head is
+ * paired with itself over two adjacent query blocks in the same launch);
+ * other bf16 shapes run one query head per workgroup.
  */
 rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* row_count, const int32_t* col_idx, void* out,

@@ -10,6 +10,7 @@ import torch
 
 import dynamic_block_sparse_rr_amd as rr
 from synthetic.gen import Workload, make_inputs
+from synthetic.rows import sample_rows, work_item_rows  # noqa: F401
 
 
 def say(*a):
@@ -66,11 +67,3 @@ class DeviceCase:
         torch.cuda.synchronize()
         return out.float().cpu().numpy(), rc.cpu().numpy().copy(), ci.cpu().numpy().copy()
 
-
-def sample_rows(L: int, Hq: int, B: int, n: int, seed: int) -> np.ndarray:
-    """(x, h) pairs: random ones plus block edges and the first/last token."""
-    rng = np.random.default_rng(seed)
-    xs = list(rng.integers(0, L, n))
-    xs += [0, 1, B - 1, B, L - 1, L - B, L - B - 1, L // 2]
-    hs = list(rng.integers(0, Hq, len(xs)))
-    return np.array(list(zip(xs, hs)), np.int32)

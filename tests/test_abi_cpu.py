@@ -178,3 +178,64 @@ def test_decode_checks_on_host():
     assert lib.rr_pool_keys(ctypes.byref(p), ok, None, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_pool_keys(ctypes.byref(base(S=48)), ok, ok, 0) == rr.RR_ERR_INVALID_ARG
     assert lib.rr_decode_workspace_bytes(None) == 0
+
+
+class _NoLibrary:
+    """Stands in for the loaded library: any use of it fails the test."""
+
+    def __getattr__(self, name):
+        raise AssertionError("the call reached the library (%s)" % name)
+
+
+def test_binding_checks_tensors_before_the_library(monkeypatch):
+    import torch
+
+    monkeypatch.setattr(rr, "_lib", _NoLibrary())
+    p = base(L=256, Hq=4, Hkv=2)
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    q, k, v, out = bf(256, 4, 128), bf(256, 2, 128), bf(256, 2, 128), bf(256, 4, 128)
+    rc, ci = i32(4, 2), i32(4, 2, 2)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    cases = [
+        (lambda: rr.rr_pattern_search(p, q.float(), k, rc, ci, None, ws), "q: expected dtype"),
+        (lambda: rr.rr_pattern_search(p, q, k[:100], rc, ci, None, ws), "k: expected at least"),
+        (lambda: rr.rr_pattern_search(p, q, k, rc.long(), ci, None, ws), "row_count: expected dtype"),
+        (lambda: rr.rr_pattern_search(p, q, k, rc, ci, bf(4, 2, 2), ws), "block_mass: expected dtype"),
+        (lambda: rr.rr_block_sparse_attn(p, q, k, v, rc, ci[:1], out, ws), "col_idx: expected at least"),
+        (lambda: rr.rr_block_sparse_attn(p, q, k, v, rc, ci, out[:10], ws), "out: expected at least"),
+        (lambda: rr.rr_prefill(p, q, k, v.float(), out, rc, ci, ws), "v: expected dtype"),
+        (lambda: rr.rr_mass_recall(p, q, k, rc, ci, torch.zeros(3)), "recall: expected at least"),
+        (lambda: rr.rr_share_group_lists(p, rc, ci, rc, i32(3)), "shared_col_idx: expected at least"),
+        (lambda: rr.rr_pattern_search_heads(p, q, k, torch.zeros(2), rc, ci, None, ws), "tau_per_head"),
+        (lambda: rr.rr_prefill_varlen(p, [128, 128], q, k, v, out, i32(7), ci, ws), "row_count: expected at least"),
+        (lambda: rr.rr_decode(p, bf(3, 128), k, v, bf(4, 128), i32(4), i32(4, 2), None, ws), "q: expected at least"),
+        (lambda: rr.rr_decode_attend(p, bf(4, 128), k, v, i32(4), i32(4, 2), bf(4, 128).float(), ws),
+         "out: expected dtype"),
+        (lambda: rr.rr_pool_keys(p, k, bf(3, 2, 128)), "kbar: expected at least"),
+        (lambda: rr.rr_pattern_search(p, q, k, rc, ci, None, ws, ws_bytes=17), "ws_bytes"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            call()
+
+
+def test_valid_calls_without_a_device_return_hip_error():
+    """Arguments that pass every host check reach the HIP runtime, which has
+    no device here: the library returns RR_ERR_HIP instead of crashing. The
+    addresses are fake, so this runs only where no GPU is visible."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: fake device addresses must not reach a kernel")
+    lib = rr.load()
+    ok = 1 << 20
+    p = base(L=1024, Hq=4, Hkv=2)
+    need = rr.rr_workspace_bytes(p)
+    dneed = rr.rr_decode_workspace_bytes(p)
+    assert lib.rr_pattern_search(ctypes.byref(p), ok, ok, ok, ok, None, ok, need, None) == rr.RR_ERR_HIP
+    assert lib.rr_block_sparse_attn(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, need, None) == rr.RR_ERR_HIP
+    assert lib.rr_prefill(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, need, None) == rr.RR_ERR_HIP
+    assert lib.rr_mass_recall(ctypes.byref(p), ok, ok, ok, ok, ok, None) == rr.RR_ERR_HIP
+    assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, None, ok, ok, ok, None, ok, dneed, None) == rr.RR_ERR_HIP
+    assert lib.rr_pool_keys(ctypes.byref(p), ok, ok, None) == rr.RR_ERR_HIP
