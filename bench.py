@@ -84,22 +84,29 @@ def search_logits(w, rows=None) -> int:
     return n * w.Hq
 
 
-def cpu_baseline(w, q, k, v, rc, ci, f_comp, seconds_hint=20.0):
-    """The oracle timed on a bounded sample, extrapolated to the whole step."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or 'unknown'."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, q, k, v, rc, ci, f_comp, n_attn_rows=8192):
+    """The oracle on the host cores: the whole search, and attention on a
+    bounded sample of (token, head) rows scaled to the whole step by FLOPs."""
     import oracle
     from synthetic.rows import sample_rows
 
     cores = oracle.max_threads()
-    rows_i = sorted({w.nb // 4, w.nb // 2, (3 * w.nb) // 4})
-    mask = np.zeros((w.Hq, w.nb), bool)
-    mask[:, rows_i] = True
     t0 = time.perf_counter()
-    oracle.search(q, k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=w.dtype == "bf16",
-                  extras=False, row_mask=mask)
+    oracle.search(q, k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=w.dtype == "bf16", extras=False)
     t_search = time.perf_counter() - t0
-    search_scale = search_logits(w) / max(1, search_logits(w, rows_i))
 
-    srows = sample_rows(w.L, w.Hq, w.B, 504, seed=11)
+    srows = sample_rows(w.L, w.Hq, w.B, n_attn_rows, seed=11)
     f_sample = 0.0
     for x, h in srows:
         i = x // w.B
@@ -109,17 +116,38 @@ def cpu_baseline(w, q, k, v, rc, ci, f_comp, seconds_hint=20.0):
     t0 = time.perf_counter()
     oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=srows)
     t_attn = time.perf_counter() - t0
-    est = t_search * search_scale + t_attn * (f_comp / f_sample)
+    est = t_search + t_attn * (f_comp / f_sample)
     return {
         "value": f_comp / est / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": ("search rows i in %s for all %d heads (%.2fs, x%.1f to the full search) + "
-                   "attention of %d sampled (token, head) rows on the GPU's block lists (%.2fs, "
-                   "x%.0f by computed FLOPs); extrapolated full step %.0f s"
-                   % (rows_i, w.Hq, t_search, search_scale, len(srows), t_attn, f_comp / f_sample, est)),
+        "cpu_model": cpu_model(),
+        "sample": ("the whole search (%.2fs) + attention of %d sampled (token, head) rows on the GPU's block "
+                   "lists (%.2fs, x%.0f to the whole attention by computed FLOPs); full step %.0f s with the "
+                   "attention extrapolated" % (t_search, len(srows), t_attn, f_comp / f_sample, est)),
+        "search_s": round(t_search, 3),
+        "attn_sample_s": round(t_attn, 3),
     }
+
+
+def measured_peaks():
+    """Run ./peak (peak.hip: MFMA and HBM rates measured on this GPU) in a child
+    process and return its summary dict, or None if it is not built or fails."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "peak")
+    if not os.path.exists(exe):
+        log("peak is not built (python -c 'import __graft_entry__ as g; g.build()'): measured peaks omitted")
+        return None
+    r = subprocess.run([exe, "all"], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log("peak failed (%d): %s" % (r.returncode, r.stderr.strip()[-300:]))
+        return None
+    for line in r.stdout.splitlines():
+        if line.startswith('{"summary"'):
+            return json.loads(line)["summary"]
+    return None
 
 
 # ragged sequence lengths of the packed batch (none a multiple of B = 128), 131,072 tokens in all
@@ -304,8 +332,10 @@ def main():
                     help="also time steps that each follow a 1 GiB buffer write (flushes the 256 MiB MALL); "
                          "reported as cold_* fields, events only")
     ap.add_argument("--hbm-ceiling", action="store_true",
-                    help="run the hbm_read probe: plain and block-walk reads of a K/V cache of the workload's "
+                    help="run peak.hip's cache probe: plain and block-walk reads of a K/V cache of the workload's "
                          "shape, the practical read ceiling of the decode attention")
+    ap.add_argument("--no-peak", action="store_true",
+                    help="skip the measured MFMA/HBM peaks (peak.hip) that the roofline also divides by")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
                          "scaling HBM byte counters")
@@ -316,14 +346,20 @@ def main():
         from synthetic.gen import workload as wl
 
         w = wl(args.workload)
-        probe = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "hbm_read")
+        probe = os.path.join(ROOT, "peak")
         if not os.path.exists(probe):
-            raise SystemExit("hbm_read is not built: run python -m dynamic_block_sparse_rr_amd.build")
-        sys.exit(subprocess.run([probe, str(w.L), str(w.Hkv)]).returncode)
+            raise SystemExit("peak is not built: run python -c 'import __graft_entry__ as g; g.build()'")
+        sys.exit(subprocess.run([probe, "cache", str(w.L), str(w.Hkv)]).returncode)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the operator runs on a single device "
               "(sharding it across GPUs is a design note, not implemented).", file=sys.stderr)
         sys.exit(2)
+
+    peaks = None
+    if not (args.no_peak or args.varlen or args.decode):
+        peaks = measured_peaks()  # a child process, before this one touches the GPU
+        if peaks:
+            log("measured peaks: " + json.dumps(peaks))
 
     import torch
 
@@ -491,6 +527,17 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
                      "kernel": "bf16 block-sparse attention (timed with the V re-layout pass of the same call)"},
     }
+    if peaks:
+        key = "mfma_bf16_reg_2w_TFLOPs" if w.dtype == "bf16" else "mfma_f32_reg_2w_TFLOPs"
+        mp = float(peaks[key])
+        line["roofline"]["peak_measured"] = mp
+        line["roofline"]["frac_measured"] = round(attn_tflops / mp, 4) if mp > 0 else None
+        line["roofline"]["peak_measured_kind"] = (
+            "peak.hip on this GPU: %s MFMA with register operands, two waves per SIMD" %
+            ("32x32x16 bf16" if w.dtype == "bf16" else "32x32x2 fp32"))
+        if w.dtype == "bf16":
+            line["roofline"]["peak_lds_fed_measured"] = float(peaks["mfma_bf16_lds_2w_TFLOPs"])
+        line["measured_peaks"] = peaks
     tr = measured_traffic(w.name, tau)
     if tr is not None:
         line["roofline"]["traffic"] = tr[0]

@@ -1,5 +1,4 @@
-"""Compile the gfx950 HIP library librr_attn.so in-tree with hipcc (and the
-hbm_read probe program that bench.py --hbm-ceiling runs).
+"""Compile the gfx950 HIP library librr_attn.so in-tree with hipcc.
 
 Usage: python -m dynamic_block_sparse_rr_amd.build
 """
@@ -16,7 +15,6 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librr_attn.so")
 SOURCES = ["rr_host.cpp", "search.hip", "attn.hip", "recall.hip", "decode.hip"]
 ARCH = "gfx950"
-PROBE = os.path.join(PKG, "hbm_read")
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
@@ -43,14 +41,6 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed with status %d" % r.returncode)
     os.replace(tmp, LIB)
-    ptmp = PROBE + ".tmp%d" % os.getpid()
-    pflags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
-    r = subprocess.run([hipcc(), *pflags, os.path.join(CSRC, "hbm_read.hip"), "-o", ptmp], capture_output=True,
-                       text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed with status %d (hbm_read)" % r.returncode)
-    os.replace(ptmp, PROBE)
     return LIB
 
 
