@@ -24,3 +24,12 @@ def rr_lib():
 
     rr.load()
     return rr
+
+
+def pytest_terminal_summary(terminalreporter):
+    from tests import report
+
+    if report.LINES:
+        terminalreporter.write_sep("-", "workload parity: block-list rows by class, attention rows compared")
+        for line in report.LINES:
+            terminalreporter.write_line(line)

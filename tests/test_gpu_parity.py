@@ -20,7 +20,7 @@ import pytest
 
 import oracle
 from synthetic.gen import Workload, workload
-from tests import checker, oracle_cache
+from tests import checker, oracle_cache, report
 from tests.gpu_cases import DeviceCase, sample_rows, say, work_item_rows
 
 pytestmark = pytest.mark.gpu
@@ -143,6 +143,8 @@ def _workload_case(name, tau):
     res = check_lists(w, tau, rc, ci, orc)
     rows_checked = res["exact"] + res["letter"] + res["near_tie"] + res["fail"]
     say(f"  rows compared {rows_checked} of {w.Hq * w.nb}")
+    line = (f"{name} tau={tau}: rows {rows_checked} of {w.Hq * w.nb}: exact {res['exact']} "
+            f"letter {res['letter']} near_tie {res['near_tie']} fail {res['fail']}")
     assert rows_checked == w.Hq * w.nb
     keep = rc.sum() / (w.Hq * w.nb * (w.nb + 1) / 2)
     say(f"  keep fraction {keep:.4f}")
@@ -166,6 +168,8 @@ def _workload_case(name, tau):
         got = out[srows[:, 0], srows[:, 1]]
         mx, mean = checker.output_errors(got, want)
         say(f"  attention ({len(srows)} rows) max-abs {mx:.3e} mean-abs {mean:.3e}")
+    nrows = w.L * w.Hq if w.L <= 1024 else len(srows)
+    report.record(line + f"; attention {nrows} (token, head) rows max-abs {mx:.2e} mean-abs {mean:.2e}")
     assert mx <= tmax and mean <= tmean
     return res
 
