@@ -89,6 +89,8 @@ def load():
         lib.rr_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.rr_decode.argtypes = [PP, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.rr_decode.restype = ctypes.c_int
+        lib.rr_decode_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P]
+        lib.rr_decode_noalloc.restype = ctypes.c_int
         lib.rr_decode_attend.argtypes = [PP, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.rr_decode_attend.restype = ctypes.c_int
         lib.rr_pool_keys.argtypes = [PP, P, P, P]
@@ -295,6 +297,17 @@ def rr_decode(p, q, k, v, out, row_count, col_idx, block_mass, ws, ws_bytes=None
     _check("rr_decode", load().rr_decode(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), _ptr(out), _ptr(row_count), _ptr(col_idx),
         _ptr(block_mass), _ptr(ws), nws, _stream(stream)))
+
+
+RR_DECODE_NOALLOC_MAX_WS = 32 << 20  # bytes of the library's own decode workspace per GPU
+
+
+def rr_decode_noalloc(p, q, k, v, out, row_count, col_idx, block_mass=None, stream=None, kbar=None):
+    """rr_decode with the library's own workspace: allocates nothing."""
+    _check_decode(p, q, k, v, out, row_count, col_idx, block_mass, kbar)
+    _check("rr_decode_noalloc", load().rr_decode_noalloc(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kbar), _ptr(out), _ptr(row_count), _ptr(col_idx),
+        _ptr(block_mass), _stream(stream)))
 
 
 def rr_decode_attend(p, q, k, v, row_count, col_idx, out, ws, ws_bytes=None, stream=None):

@@ -11,6 +11,8 @@
 #include "rr_attn.h"
 #include "rr_kernels.h"
 
+static_assert(rr::kStaticWorkspaceBytes == RR_DECODE_NOALLOC_MAX_WS, "header and library disagree");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -315,9 +317,9 @@ rr_status rr_pool_keys(const rr_problem* p, const void* k, void* kbar, void* str
   return hip_status(rr::launch_pool_keys(g, k, kbar, false, static_cast<hipStream_t>(stream)));
 }
 
-rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar, void* out,
-                    int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
-                    void* stream) {
+static rr_status decode_step(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar,
+                             void* out, int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws,
+                             size_t ws_bytes, bool static_ws, void* stream) {
   rr::Geometry g;
   rr_status s = make_geometry(p, &g);
   if (s != RR_OK) return s;
@@ -328,10 +330,15 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
   if (block_mass && !aligned16(block_mass)) return RR_ERR_INVALID_ARG;
   if (kbar && !aligned16(kbar)) return RR_ERR_INVALID_ARG;
   const DecodeWorkspace w = decode_layout(g);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (static_ws) {  // the library's own buffer on the stream's device
+    if (w.total > rr::kStaticWorkspaceBytes) return RR_ERR_WORKSPACE;
+    if (rr::static_workspace(st, &ws) != hipSuccess) return RR_ERR_HIP;
+    ws_bytes = rr::kStaticWorkspaceBytes;
+  }
   if (!ws || !aligned16(ws) || ws_bytes < w.total) return RR_ERR_WORKSPACE;
   uint8_t* base = static_cast<uint8_t*>(ws);
   float* mass = block_mass ? block_mass : reinterpret_cast<float*>(base + w.mass);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (!kbar) {  // pool the cache's keys here
     e = rr::launch_pool_keys(g, k, base + w.kbar, false, st);
@@ -349,6 +356,17 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
     e = rr::launch_decode_attn(g, q, k, v, row_count, col_idx, sel, w.nbp, reinterpret_cast<float*>(base + w.part),
                                out, st);
   return hip_status(e);
+}
+
+rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar, void* out,
+                    int32_t* row_count, int32_t* col_idx, float* block_mass, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return decode_step(p, q, k, v, kbar, out, row_count, col_idx, block_mass, ws, ws_bytes, false, stream);
+}
+
+rr_status rr_decode_noalloc(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar,
+                            void* out, int32_t* row_count, int32_t* col_idx, float* block_mass, void* stream) {
+  return decode_step(p, q, k, v, kbar, out, row_count, col_idx, block_mass, nullptr, 0, true, stream);
 }
 
 rr_status rr_decode_attend(const rr_problem* p, const void* q, const void* k, const void* v, const int32_t* row_count,

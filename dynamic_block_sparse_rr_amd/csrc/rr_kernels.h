@@ -61,6 +61,11 @@ hipError_t launch_decode_attn(const Geometry& g, const void* q, const void* k, c
                               const int32_t* row_count, const int32_t* col_idx, const uint8_t* sel, int nbp,
                               float* part, void* out, hipStream_t st);
 
+// The device buffer of rr_decode_noalloc (static_ws.hip): kStaticWorkspaceBytes
+// per GPU, its address on the device that runs `st` (looked up once per device).
+constexpr size_t kStaticWorkspaceBytes = 32u << 20;
+hipError_t static_workspace(hipStream_t st, void** ptr);
+
 // Kernel-side limits checked by the host before any launch.
 constexpr int kMaxSelectBlocks = 8192;  // LDS sort capacity of the select kernel (nb): 12 B per key
 

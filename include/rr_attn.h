@@ -228,6 +228,25 @@ rr_status rr_decode(const rr_problem* p, const void* q, const void* k, const voi
 rr_status rr_decode_attend(const rr_problem* p, const void* q, const void* k, const void* v, const int32_t* row_count,
                            const int32_t* col_idx, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * rr_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, kernels and results as rr_decode, without ws / ws_bytes: the
+ * workspace is a buffer the library owns, RR_DECODE_NOALLOC_MAX_WS bytes on
+ * every GPU it runs on, held from the library's load until the process ends.
+ * The call allocates nothing. A problem whose rr_decode_workspace_bytes(p)
+ * exceeds RR_DECODE_NOALLOC_MAX_WS returns RR_ERR_WORKSPACE and launches
+ * nothing (for the 8B-shaped layer, 32 query and 8 KV heads of 128 bf16
+ * channels: every supported cache length with kbar given; up to about 245K
+ * tokens with the keys pooled inside the call). Every call on one GPU
+ * shares that GPU's buffer: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls ordered on
+ * one stream are safe. No state carries over between calls.
+ */
+#define RR_DECODE_NOALLOC_MAX_WS ((size_t)32 << 20)
+rr_status rr_decode_noalloc(const rr_problem* p, const void* q, const void* k, const void* v, const void* kbar,
+                            void* out, int32_t* row_count, int32_t* col_idx, float* block_mass, void* stream);
+
 /* The pooled keys of rr_pattern_search's first step, on their own: kbar
  * [ceil(L/S)][Hkv][d] in p->dtype receives, per stride of S tokens (the last
  * possibly short), the float32 mean of its keys rounded to the dtype. */

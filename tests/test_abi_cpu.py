@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol():
     assert names == sorted(["rr_workspace_bytes", "rr_pattern_search", "rr_block_sparse_attn",
                             "rr_prefill", "rr_mass_recall", "rr_share_group_lists", "rr_status_string",
                             "rr_version", "rr_pattern_search_heads", "rr_workspace_bytes_varlen",
-                            "rr_prefill_varlen", "rr_decode_workspace_bytes", "rr_decode", "rr_decode_attend", "rr_pool_keys"])
+                            "rr_prefill_varlen", "rr_decode_workspace_bytes", "rr_decode", "rr_decode_attend", "rr_pool_keys",
+                            "rr_decode_noalloc"])
     lib = ctypes.CDLL(rr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -239,3 +240,20 @@ def test_valid_calls_without_a_device_return_hip_error():
     assert lib.rr_mass_recall(ctypes.byref(p), ok, ok, ok, ok, ok, None) == rr.RR_ERR_HIP
     assert lib.rr_decode(ctypes.byref(p), ok, ok, ok, None, ok, ok, ok, None, ok, dneed, None) == rr.RR_ERR_HIP
     assert lib.rr_pool_keys(ctypes.byref(p), ok, ok, None) == rr.RR_ERR_HIP
+
+
+def test_noalloc_decode_checks_on_host():
+    """rr_decode_noalloc validates like rr_decode and refuses problems whose
+    workspace exceeds the library's own buffer, before any HIP call."""
+    lib = rr.load()
+    ok = 1 << 20
+    assert rr.RR_DECODE_NOALLOC_MAX_WS == 32 << 20
+    fits = base(L=131072)
+    assert rr.rr_decode_workspace_bytes(fits) <= rr.RR_DECODE_NOALLOC_MAX_WS
+    big = base(L=262144)  # pooled keys alone take 32 MiB
+    assert rr.rr_decode_workspace_bytes(big) > rr.RR_DECODE_NOALLOC_MAX_WS
+    assert lib.rr_decode_noalloc(ctypes.byref(big), ok, ok, ok, None, ok, ok, ok, None, 0) == rr.RR_ERR_WORKSPACE
+    assert lib.rr_decode_noalloc(ctypes.byref(fits), None, ok, ok, None, ok, ok, ok, None, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode_noalloc(ctypes.byref(fits), ok, ok, ok, ok + 8, ok, ok, ok, None, 0) == rr.RR_ERR_INVALID_ARG
+    assert lib.rr_decode_noalloc(ctypes.byref(base(d=96)), ok, ok, ok, None, ok, ok, ok, None, 0) == rr.RR_ERR_UNSUPPORTED
+    assert lib.rr_decode_noalloc(None, ok, ok, ok, None, ok, ok, ok, None, 0) == rr.RR_ERR_INVALID_ARG
