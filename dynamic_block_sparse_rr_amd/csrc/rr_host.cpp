@@ -34,8 +34,10 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
   if (p->B != 64 && p->B != 128) return RR_ERR_UNSUPPORTED;
   const int r = p->B / p->S;
   if (!is_pow2(p->S) || r < 2 || r > 32) return RR_ERR_UNSUPPORTED;
-  const int nb = (p->L + p->B - 1) / p->B;  // the last block may be short
-  if (nb > rr::kMaxSelectBlocks) return RR_ERR_UNSUPPORTED;
+  // the last block may be short (64-bit: L near INT_MAX must not overflow)
+  const long long nbl = ((long long)p->L + p->B - 1) / p->B;
+  if (nbl > rr::kMaxSelectBlocks) return RR_ERR_UNSUPPORTED;
+  const int nb = (int)nbl;
   if ((long long)p->Hq * nb > (1LL << 30)) return RR_ERR_UNSUPPORTED;
   g->L = p->L;
   g->Hq = p->Hq;
@@ -44,7 +46,7 @@ rr_status make_geometry(const rr_problem* p, rr::Geometry* g) {
   g->S = p->S;
   g->B = p->B;
   g->nb = nb;
-  g->ns = (p->L + p->S - 1) / p->S;  // the last stride may be short
+  g->ns = (int)(((long long)p->L + p->S - 1) / p->S);  // the last stride may be short
   g->r = r;
   g->G = p->Hq / p->Hkv;
   g->causal = p->causal;

@@ -1,0 +1,130 @@
+// CPU stand-ins for the kernel launches of the C-ABI library, so that its
+// host runtime (argument checks, workspace layout, the varlen and decode
+// sequencing in rr_host.cpp) can be built with g++ under AddressSanitizer and
+// UndefinedBehaviorSanitizer and driven without a GPU (tests/sanitize/
+// host_driver.cpp). Every launch records its call and checks that each
+// buffer the host carved out of the caller's workspace lies inside it.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "rr_kernels.h"
+#include "stub_state.h"
+
+StubState g_stub;
+
+static void in_ws(const void* p, size_t bytes, const char* what) {
+  const char* b = static_cast<const char*>(g_stub.ws);
+  const char* q = static_cast<const char*>(p);
+  if (!b || q < b || q + bytes > b + g_stub.ws_bytes) {
+    fprintf(stderr, "workspace range violated: %s (%zu bytes at offset %td of %zu)\n", what, bytes, q - b,
+            g_stub.ws_bytes);
+    abort();
+  }
+}
+
+static size_t esz(const rr::Geometry& g) { return g.bf16 ? 2 : 4; }
+
+namespace rr {
+
+hipError_t launch_pool_keys(const Geometry& g, const void*, void* kbar, bool, hipStream_t) {
+  ++g_stub.calls;
+  if (g_stub.ws) {
+    const char* b = static_cast<const char*>(g_stub.ws);
+    const char* q = static_cast<const char*>(kbar);
+    if (q >= b && q < b + g_stub.ws_bytes) in_ws(kbar, (size_t)g.ns * g.Hkv * g.d * esz(g), "pooled keys");
+  }
+  return g_stub.fail_launch ? hipErrorLaunchFailure : hipSuccess;
+}
+
+hipError_t launch_search(const Geometry& g, const void*, const void* kbar, float* mass, hipStream_t) {
+  ++g_stub.calls;
+  in_ws(kbar, (size_t)g.ns * g.Hkv * g.d * esz(g), "pooled keys (search)");
+  if (!g_stub.user_mass) in_ws(mass, (size_t)g.Hq * g.nb * g.nb * sizeof(float), "block masses");
+  return hipSuccess;
+}
+
+hipError_t launch_select(const Geometry& g, const float* mass, int, int32_t*, int32_t*, const float*, hipStream_t) {
+  ++g_stub.calls;
+  if (!g_stub.user_mass) in_ws(mass, (size_t)g.Hq * g.nb * g.nb * sizeof(float), "block masses (select)");
+  return hipSuccess;
+}
+
+hipError_t launch_union_lists(const Geometry&, const int32_t*, const int32_t*, int32_t*, int32_t*, hipStream_t) {
+  ++g_stub.calls;
+  return hipSuccess;
+}
+
+hipError_t launch_transpose_v(const Geometry& g, const void*, void* vt, int32_t* queues, hipStream_t) {
+  ++g_stub.calls;
+  in_ws(vt, (size_t)g.nb * g.B * g.Hkv * g.d * esz(g), "V re-layout");
+  in_ws(queues, kAttnQueues * sizeof(int32_t), "work-queue counters");
+  return hipSuccess;
+}
+
+hipError_t launch_attention(const Geometry& g, const void*, const void*, const void*, const void* vt,
+                            int32_t* queues, const int32_t*, const int32_t*, void*, hipStream_t) {
+  ++g_stub.calls;
+  if (g.bf16) {
+    in_ws(vt, (size_t)g.nb * g.B * g.Hkv * g.d * esz(g), "V re-layout (attention)");
+    in_ws(queues, kAttnQueues * sizeof(int32_t), "work-queue counters (attention)");
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_recall(const Geometry&, const void*, const void*, const int32_t*, const int32_t*, float*,
+                         hipStream_t) {
+  ++g_stub.calls;
+  return hipSuccess;
+}
+
+// the decode split / chunk counts only size workspace parts here
+bool decode_grouped(const Geometry& g) { return g.bf16 && g.G <= 8; }
+int decode_splits(const Geometry& g) { return (g.nb + 15) / 16; }
+int decode_chunks(const Geometry& g) { return (g.ns + 255) / 256; }
+
+hipError_t launch_decode_scores(const Geometry& g, const void*, const void* kbar, float* bsum, float* zpart,
+                                hipStream_t) {
+  ++g_stub.calls;
+  if (!g_stub.user_kbar) in_ws(kbar, (size_t)g.ns * g.Hkv * g.d * esz(g), "decode pooled keys");
+  in_ws(bsum, (size_t)g.Hq * g.nb * sizeof(float), "decode block sums");
+  in_ws(zpart, (size_t)g.Hq * decode_chunks(g) * 2 * sizeof(float), "decode chunk partials");
+  return hipSuccess;
+}
+
+hipError_t launch_decode_select(const Geometry& g, const float* bsum, const float* zpart, float* mass, int32_t*,
+                                int32_t*, uint8_t* sel, int nbp, hipStream_t) {
+  ++g_stub.calls;
+  in_ws(bsum, (size_t)g.Hq * g.nb * sizeof(float), "decode block sums (select)");
+  in_ws(zpart, (size_t)g.Hq * decode_chunks(g) * 2 * sizeof(float), "decode chunk partials (select)");
+  if (!g_stub.user_mass) in_ws(mass, (size_t)g.Hq * g.nb * sizeof(float), "decode masses");
+  in_ws(sel, (size_t)g.Hq * nbp, "decode flags");
+  if (nbp < g.nb) abort();
+  return hipSuccess;
+}
+
+hipError_t launch_lists_to_flags(const Geometry& g, const int32_t*, const int32_t*, uint8_t* sel, int nbp,
+                                 hipStream_t) {
+  ++g_stub.calls;
+  in_ws(sel, (size_t)g.Hq * nbp, "decode flags (lists)");
+  return hipSuccess;
+}
+
+hipError_t launch_decode_attn(const Geometry& g, const void*, const void*, const void*, const int32_t*,
+                              const int32_t*, const uint8_t* sel, int nbp, float* part, void*, hipStream_t) {
+  ++g_stub.calls;
+  in_ws(sel, (size_t)g.Hq * nbp, "decode flags (attention)");
+  in_ws(part, (size_t)g.Hq * decode_splits(g) * (g.d + 2) * sizeof(float), "decode split partials");
+  return hipSuccess;
+}
+
+// the library's own decode buffer: a host allocation here (never dereferenced)
+hipError_t static_workspace(hipStream_t, void** ptr) {
+  static void* buf = nullptr;
+  if (!buf) buf = aligned_alloc(256, kStaticWorkspaceBytes);
+  *ptr = buf;
+  g_stub.ws = buf;
+  g_stub.ws_bytes = kStaticWorkspaceBytes;
+  return hipSuccess;
+}
+
+}  // namespace rr

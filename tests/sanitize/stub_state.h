@@ -1,0 +1,13 @@
+// State shared by the launch stand-ins and the host driver (sanitizer build).
+#pragma once
+#include <stddef.h>
+
+struct StubState {
+  const void* ws = nullptr;  // the workspace of the current call
+  size_t ws_bytes = 0;
+  bool user_mass = false;    // the caller passed its own block-mass buffer
+  bool user_kbar = false;    // the caller passed its own pooled keys (decode)
+  bool fail_launch = false;  // make the first launch report a failure
+  long calls = 0;
+};
+extern StubState g_stub;
