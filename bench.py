@@ -95,24 +95,62 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, q, k, v, rc, ci, f_comp, n_attn_rows=8192):
+def _row_flops(w, rc, ci, rows) -> float:
+    """Computed FLOPs (QK and PV) of the given (token, head) output rows on these lists."""
+    f = 0.0
+    for x, h in rows:
+        i = x // w.B
+        js = ci[h, i, : rc[h, i]]
+        keys = int(sum(min(w.B, x - j * w.B + 1) if (w.causal and j == i) else min(w.B, w.L - j * w.B)
+                       for j in js))
+        f += 4.0 * w.d * keys
+    return f
+
+
+def cpu_baseline(w, q, k, v, rc, ci, f_comp, tau, n_attn_rows=8192, full=False):
     """The oracle on the host cores: the whole search, and attention on a
-    bounded sample of (token, head) rows scaled to the whole step by FLOPs."""
+    bounded sample of (token, head) rows scaled to the whole step by FLOPs.
+    full: the whole attention up to 32K tokens; beyond, every row of four
+    heads spread over the KV heads, scaled by the FLOPs of their lists."""
     import oracle
     from synthetic.rows import sample_rows
 
     cores = oracle.max_threads()
     t0 = time.perf_counter()
-    oracle.search(q, k, S=w.S, B=w.B, tau=0.9, causal=w.causal, round_bf16=w.dtype == "bf16", extras=False)
+    oracle.search(q, k, S=w.S, B=w.B, tau=tau, causal=w.causal, round_bf16=w.dtype == "bf16", extras=False)
     t_search = time.perf_counter() - t0
 
+    if full and w.L > 32768:
+        heads = [j * (w.Hq // 4) for j in range(4)]
+        rows = np.array([(x, h) for h in heads for x in range(w.L)], np.int32)
+        f_sub = 0.0
+        for h in heads:
+            f_sub += computed_flops(rc[h:h + 1], ci[h:h + 1], w.B, w.d, w.causal)[0]
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=rows)
+        t_attn = time.perf_counter() - t0
+        est = t_search + t_attn * (f_comp / f_sub)
+        return {
+            "value": f_comp / est / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": ("the whole search (%.2fs) + attention of every row of heads %s (%.2fs, x%.2f to the whole "
+                       "attention by computed FLOPs); full step %.0f s with the attention extrapolated"
+                       % (t_search, heads, t_attn, f_comp / f_sub, est)),
+            "search_s": round(t_search, 3), "attn_heads_s": round(t_attn, 3), "step_s_est": round(est, 1),
+        }
+    if full or w.L * w.Hq <= n_attn_rows:  # the whole attention, nothing extrapolated
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal)
+        t_attn = time.perf_counter() - t0
+        est = t_search + t_attn
+        return {
+            "value": f_comp / est / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "the whole step: search (%.3fs) and attention (%.3fs) in full" % (t_search, t_attn),
+            "search_s": round(t_search, 4), "attn_s": round(t_attn, 4),
+        }
     srows = sample_rows(w.L, w.Hq, w.B, n_attn_rows, seed=11)
-    f_sample = 0.0
-    for x, h in srows:
-        i = x // w.B
-        js = ci[h, i, : rc[h, i]]
-        keys = int(sum(min(w.B, x - j * w.B + 1) if (w.causal and j == i) else w.B for j in js))
-        f_sample += 4.0 * w.d * keys
+    f_sample = _row_flops(w, rc, ci, srows)
     t0 = time.perf_counter()
     oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=srows)
     t_attn = time.perf_counter() - t0
@@ -316,6 +354,9 @@ def main():
     ap.add_argument("--workload", default="llama8b_L128k")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-full", action="store_true",
+                    help="time the oracle's whole step (up to 32K tokens) or every row of four heads (longer "
+                         "layers) instead of a bounded sample: minutes at 64K and 128K")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--recall", action="store_true",
                     help="also run rr_mass_recall on the produced lists: the full-attention softmax mass the "
@@ -525,7 +566,8 @@ def main():
         **extra,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4), "traffic": None,
-                     "kernel": "bf16 block-sparse attention (timed with the V re-layout pass of the same call)"},
+                     "kernel": ("bf16 block-sparse attention (timed with the V re-layout pass of the same call)"
+                                if w.dtype == "bf16" else "fp32 block-sparse attention on the fp32 MFMA")},
     }
     if peaks:
         key = "mfma_bf16_reg_2w_TFLOPs" if w.dtype == "bf16" else "mfma_f32_reg_2w_TFLOPs"
@@ -545,7 +587,7 @@ def main():
         line["roofline"]["algorithmic_bytes"] = tr[1]
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, rc, ci, f_comp)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, rc, ci, f_comp, tau, full=args.cpu_baseline_full)
     print(json.dumps(line), flush=True)
 
 

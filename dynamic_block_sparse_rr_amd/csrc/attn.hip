@@ -940,64 +940,172 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
 
 // ------------------------------------------------------------------ fp32 attention
 
+// float32 path on the fp32 matrix cores (v_mfma_f32_32x32x2f32). A workgroup
+// of f32_waves(D) waves (8 at d = 64, 4 at d = 128, as LDS allows) serves one
+// query head and one tile of 32 queries; wave w takes entries w, w + waves,
+// ... of the row's block list, walks each
+// selected block in 32-key subtiles staged in its own LDS area, and keeps
+// its own running maximum, sum and O; the waves' partial results are merged
+// at the end (each part rescaled to the common maximum). Per subtile:
+//   S^T = K Q^T, D/2 MFMAs: A = K (32 keys x 2 channels, one LDS float per
+//     lane, rows padded to D+1 floats so the 32 keys of a read fall in
+//     distinct banks), B = Q^T (the lane's query, two channels: registers);
+//     lane (query n, half hf) then holds keys 8*(v/4) + 4*hf + v%4, v < 16;
+//   online softmax in base 2 on those 16 scores (one cross-half exchange);
+//   O^T += Vt P^T, 16 MFMAs per 32 channels: MFMA v pairs key 8*(v/4) + v%4
+//     (lane half 0) with key 8*(v/4) + 4 + v%4 (half 1), exactly the keys the
+//     lane's P register v holds, so P is the B operand as it stands, and A
+//     reads V[that key][the lane's channel] from LDS.
+__host__ __device__ constexpr int f32_waves(int D) { return D == 64 ? 8 : 4; }
+
+template <int D>
+struct F32Lds {
+  static constexpr int F32_WAVES = f32_waves(D);
+  static constexpr int KP = D + 1;                 // padded row of a staged K or V subtile (floats)
+  static constexpr int WAVE = 2 * 32 * KP;         // floats per wave: K and V subtiles
+  static constexpr int MERGE = 32 * D + 64;        // floats per wave for the merge: O^T [D][32], m, l
+  static constexpr int PER_WAVE = WAVE > MERGE ? WAVE : MERGE;
+  static constexpr size_t BYTES = (size_t)F32_WAVES * PER_WAVE * sizeof(float);
+};
+
 template <int D, int BLK>
-__global__ void __launch_bounds__(BLK) attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                       const float* __restrict__ v,
-                                                       const int32_t* __restrict__ row_count,
-                                                       const int32_t* __restrict__ col_idx,
-                                                       float* __restrict__ out, int Hq, int Hkv, int nb,
-                                                       int causal, float cscale, int L) {
+__global__ void __launch_bounds__(f32_waves(D) * 64) attn_f32_kernel(const float* __restrict__ q,
+                                                                  const float* __restrict__ k,
+                                                                  const float* __restrict__ v,
+                                                                  const int32_t* __restrict__ row_count,
+                                                                  const int32_t* __restrict__ col_idx,
+                                                                  float* __restrict__ out, int Hq, int Hkv, int nb,
+                                                                  int causal, float cscale, int L, int ntiles) {
+  typedef F32Lds<D> Lds;
+  constexpr int KP = Lds::KP;
+  constexpr int F32_WAVES = Lds::F32_WAVES;
   extern __shared__ float smem[];
-  float* ks = smem;             // [BLK][D]
-  float* vs = smem + BLK * D;   // [BLK][D]
-  const int h = blockIdx.x % Hq;
-  const int i = nb - 1 - blockIdx.x / Hq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, half = lane >> 5;
+  // longest rows first: query tiles in decreasing order, heads adjacent
+  const int qt = ntiles - 1 - (int)blockIdx.x / Hq;
+  const int h = (int)blockIdx.x % Hq;
   const int g = h / (Hq / Hkv);
-  const int qr = threadIdx.x;
-  const int x = i * BLK + qr;
-  float qv[D], o[D];
+  const int i = qt * 32 / BLK;                  // query block of this tile
+  const int x = qt * 32 + n32;                  // this lane's query
+  float* ks = smem + wave * Lds::PER_WAVE;      // K subtile [32][KP]
+  float* vs = ks + 32 * KP;                     // V subtile [32][KP]
+
+  float qf[D / 2];  // B operand of step kk: channel 2*kk + half of the lane's query
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = x < L ? q[((size_t)x * Hq + h) * D + e] * cscale : 0.0f;
-    o[e] = 0.0f;
-  }
-  float m = -INFINITY, l = 0.0f;
+  for (int kk = 0; kk < D / 2; ++kk) qf[kk] = x < L ? q[((size_t)x * Hq + h) * D + 2 * kk + half] : 0.0f;
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
+  float mrow = -INFINITY, lrow = 0.0f;
+
   const size_t row = (size_t)h * nb + i;
   const int cnt = min(max(row_count[row], 0), nb);
-  for (int c = 0; c < cnt; ++c) {
-    const int j = min(max(col_idx[row * nb + c], 0), nb - 1);
-    if (causal && j > i) continue;
-    __syncthreads();
-    for (int n = threadIdx.x; n < BLK * D; n += BLK) {
-      const int r = n / D, e = n % D;
-      const bool in = j * BLK + r < L;  // a short last block ends at L
-      const size_t src = ((size_t)(j * BLK + r) * Hkv + g) * D + e;
-      ks[n] = in ? k[src] : 0.0f;
-      vs[n] = in ? v[src] : 0.0f;
-    }
-    __syncthreads();
-    const int ylast = min((causal && j == i) ? qr : BLK - 1, L - 1 - j * BLK);
-    for (int y = 0; y <= ylast; ++y) {
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < D; ++e) s += qv[e] * ks[y * D + e];
-      if (s > m) {
-        const float a = exp2_approx(m - s);
-        l *= a;
-#pragma unroll
-        for (int e = 0; e < D; ++e) o[e] *= a;
-        m = s;
+  const int32_t* lst = col_idx + row * nb;
+  const int jmax = causal ? i : nb - 1;
+  for (int c = wave; c < cnt; c += F32_WAVES) {
+    const int j = min(max(lst[c], 0), jmax);
+    for (int st = 0; st < BLK / 32; ++st) {
+      const int key0 = j * BLK + st * 32;  // first key of the subtile
+      // skip subtiles with no visible key for any query of the tile (wave-uniform)
+      if (key0 >= L) break;
+      if (causal && key0 > qt * 32 + 31) break;
+      // stage K and V rows key0 .. key0+31 (zeros past L)
+      for (int n = lane; n < 32 * D / 4; n += 64) {
+        const int r = n / (D / 4), c4 = n % (D / 4);
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+        if (key0 + r < L) {
+          const size_t src = ((size_t)(key0 + r) * Hkv + g) * D + c4 * 4;
+          kv = *reinterpret_cast<const float4*>(k + src);
+          vv = *reinterpret_cast<const float4*>(v + src);
+        }
+        float* kd = ks + r * KP + c4 * 4;
+        float* vd = vs + r * KP + c4 * 4;
+        kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
+        vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
       }
-      const float p = exp2_approx(s - m);
-      l += p;
+      // this wave's LDS writes are done before any of its lanes reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      f32x16 sacc = f32x16{};
 #pragma unroll
-      for (int e = 0; e < D; ++e) o[e] += p * vs[y * D + e];
+      for (int kk = 0; kk < D / 2; ++kk)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[n32 * KP + 2 * kk + half], qf[kk], sacc, 0, 0, 0);
+      // keys past the lane's query (causal) or past L are masked
+      const int klim = min(causal ? x : L - 1, L - 1);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = key0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        if (key > klim) sacc[e] = -INFINITY;
+        tmax = fmaxf(tmax, sacc[e]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(mrow, tmax * cscale);
+      const float mref = mnew == -INFINITY ? 0.0f : mnew;  // a row with nothing visible yet stays at zero
+      const float alpha = exp2_approx(mrow - mref);
+      lrow *= alpha;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+      mrow = mnew;
+      float pv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = exp2_approx(__builtin_fmaf(sacc[e], cscale, -mref));
+        lrow += pv[e];
+      }
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = 8 * (e >> 2) + 4 * half + (e & 3);
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * KP + t * 32 + n32], pv[e], oacc[t], 0, 0, 0);
+        }
+      // every lane's reads of this subtile have returned before the next one is staged
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  if (x >= L) return;
+
+  // merge the waves' parts: O^T [D][32], the maximum and the sum per query
+  __syncthreads();  // every wave is done with its K/V area
+  float* ob = smem + wave * Lds::PER_WAVE;
 #pragma unroll
-  for (int e = 0; e < D; ++e) out[((size_t)x * Hq + h) * D + e] = o[e] * inv;
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ob[(t * 32 + 8 * (e >> 2) + 4 * half + (e & 3)) * 32 + n32] = oacc[t][e];
+  const float ltot = lrow + __shfl_xor(lrow, 32);
+  if (half == 0) {
+    ob[32 * D + n32] = mrow;
+    ob[32 * D + 32 + n32] = ltot;
+  }
+  __syncthreads();
+  constexpr int TPQ = F32_WAVES * 64 / 32;  // threads per query
+  const int qq = tid / TPQ, part = tid % TPQ;
+  const int xo = qt * 32 + qq;
+  float mw[F32_WAVES], m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < F32_WAVES; ++w) {
+    mw[w] = smem[w * Lds::PER_WAVE + 32 * D + qq];
+    m = fmaxf(m, mw[w]);
+  }
+  const float mr = m == -INFINITY ? 0.0f : m;
+  float aw[F32_WAVES], l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < F32_WAVES; ++w) {
+    aw[w] = exp2_approx(mw[w] - mr);
+    l += aw[w] * smem[w * Lds::PER_WAVE + 32 * D + 32 + qq];
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (xo >= L) return;
+  constexpr int CPT = D / TPQ;  // channels per thread
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    const int ch = part * CPT + e;
+    float o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < F32_WAVES; ++w) o += aw[w] * smem[w * Lds::PER_WAVE + ch * 32 + qq];
+    out[((size_t)xo * Hq + h) * D + ch] = o * inv;
+  }
 }
 
 }  // namespace
@@ -1093,14 +1201,17 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
   float* oo = static_cast<float*>(out);
 #define RR_F32_CASE(DV, BV)                                                                       \
   if (g.d == DV && g.B == BV) {                                                                   \
-    const size_t lds = 2 * (size_t)BV * DV * sizeof(float);                                       \
+    const size_t lds = F32Lds<DV>::BYTES;                                                         \
     hipError_t fe = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_f32_kernel<DV, BV>),    \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
     if (fe != hipSuccess) return fe;                                                              \
-    attn_f32_kernel<DV, BV><<<grid, BV, lds, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
-                                                   g.nb, g.causal, cscale, g.L);                \
+    attn_f32_kernel<DV, BV><<<f32grid, f32_waves(DV) * 64, lds, st>>>(qq, kk, vv, row_count, col_idx, oo, \
+                                                                 g.Hq, g.Hkv, g.nb, g.causal, cscale, \
+                                                                 g.L, ntiles);                    \
     return hipGetLastError();                                                                     \
   }
+  const int ntiles = (g.L + 31) / 32;
+  const dim3 f32grid((unsigned)(g.Hq * ntiles));
   RR_F32_CASE(128, 128)
   RR_F32_CASE(128, 64)
   RR_F32_CASE(64, 128)
