@@ -253,7 +253,7 @@ def bench_varlen(args):
                    "B": 128, "S": 16, "tau": tau, "causal": True},
         "step_ms_median_events": round(float(np.median(ev_ms)), 3),
         "blocks_computed_pct": round(100.0 * blocks / cand, 2),
-        "note": "search + attention of every sequence, one after the other on one stream (rr_prefill_varlen)",
+        "note": "rr_prefill_varlen: the searches one after the other, the attention of all sequences in one launch",
     }
     print(json.dumps(line), flush=True)
 

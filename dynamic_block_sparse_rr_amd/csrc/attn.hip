@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "rr_kernels.h"
 
@@ -74,17 +75,38 @@ __host__ __device__ __forceinline__ int key_of_pos(int p) {
   return 8 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3);
 }
 
+// The batch table argument of the varlen launches (an empty struct otherwise).
+struct NoBatch {};
+template <bool VARLEN>
+using BatchArg = typename std::conditional<VARLEN, SeqBatch, NoBatch>::type;
+
 // ------------------------------------------------------------------ V re-layout
 
-template <int D, int BLK>
-__global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v,
-                                                          __bf16* __restrict__ vt, int Hkv, int nb, int L,
-                                                          int32_t* __restrict__ queues) {
+//
+// VARLEN: one launch re-lays out every sequence of a packed batch (SeqBatch):
+// workgroup x belongs to the sequence whose tile range holds it.
+template <int D, int BLK, bool VARLEN>
+__global__ void __launch_bounds__(256) transpose_v_kernel(const __bf16* __restrict__ v_all,
+                                                          __bf16* __restrict__ vt_all, int Hkv, int nb_all,
+                                                          int L_all, int32_t* __restrict__ queues,
+                                                          const BatchArg<VARLEN> sb) {
   // one workgroup per (g, key block j); tile BLK keys x D channels
   __shared__ uint16_t tile[BLK][D + 2];
   if (blockIdx.x == 0 && threadIdx.x < kAttnQueues) queues[threadIdx.x] = 0;  // the attention's work queues
-  const int j = blockIdx.x % nb;
-  const int g = blockIdx.x / nb;
+  const __bf16* v = v_all;
+  __bf16* vt = vt_all;
+  int nb = nb_all, L = L_all, tile_id = (int)blockIdx.x;
+  if constexpr (VARLEN) {  // the sequence of this tile (uniform)
+    int sq = 0;
+    while (sq + 1 < sb.n && tile_id >= sb.tile_off[sq + 1]) ++sq;
+    tile_id -= sb.tile_off[sq];
+    nb = sb.nb[sq];
+    L = sb.L[sq];
+    v = v_all + (size_t)sb.tok_off[sq] * Hkv * D;
+    vt = reinterpret_cast<__bf16*>(reinterpret_cast<uint8_t*>(vt_all) + sb.vt_off[sq]);
+  }
+  const int j = tile_id % nb;
+  const int g = tile_id / nb;
   const uint16_t* src = reinterpret_cast<const uint16_t*>(v);
   constexpr int CH = D / 8;  // 16-byte chunks per key row
   for (int n = threadIdx.x; n < BLK * CH; n += 256) {
@@ -700,12 +722,19 @@ __device__ __forceinline__ int claim_item(int32_t* queues, int nq, int nitems) {
 // once, and workgroups that find every queue empty exit at once. The two
 // items are two straight-line copies of the body: a loop over items makes the
 // compiler keep its whole register budget and spill.
-template <int D, int BLK, bool ODD>
+//
+// VARLEN: the launch covers a packed batch of sequences (SeqBatch): item x
+// belongs to the sequence whose item range holds it, and is decoded as that
+// sequence's own item; the tensors, lists and lengths are that sequence's.
+// Each range starts at a multiple of 16, so a sequence's items keep the XCD
+// split of pair_item / odd_item; the padding items past a sequence's own
+// count exit at once.
+template <int D, int BLK, bool ODD, bool VARLEN>
 __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_pp_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ vt,
-    const int32_t* __restrict__ row_count, const int32_t* __restrict__ col_idx, __bf16* __restrict__ out,
-    int Hq, int Hkv, int nb, int causal, float cscale, int L, int32_t* __restrict__ queues, int nq, int nitems,
-    int two) {
+    const __bf16* __restrict__ q_all, const __bf16* __restrict__ k_all, const __bf16* __restrict__ vt_all,
+    const int32_t* __restrict__ rc_all, const int32_t* __restrict__ ci_all, __bf16* __restrict__ out_all,
+    int Hq, int Hkv, int nb_all, int causal, float cscale, int L_all, int32_t* __restrict__ queues, int nq,
+    int nitems, int two, const BatchArg<VARLEN> sb) {
   typedef PairCtx<D, BLK> C;
   constexpr int KCH = C::KCH;
   constexpr int MT = C::MT;
@@ -715,7 +744,31 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
   __shared__ __attribute__((aligned(1024))) uint8_t lds_v1[C::TILE];
 
   // one work item; returns early (per thread) where the item or a row ends
-  auto process = [&](const int item) __attribute__((always_inline)) {
+  auto process = [&](const int item_in) __attribute__((always_inline)) {
+    const __bf16* q = q_all;
+    const __bf16* k = k_all;
+    const __bf16* vt = vt_all;
+    const int32_t* row_count = rc_all;
+    const int32_t* col_idx = ci_all;
+    __bf16* out = out_all;
+    int nb = nb_all, L = L_all, item = item_in;
+    if constexpr (VARLEN) {  // the sequence of this item, and the item inside it (uniform)
+      int sq = 0;
+      while (sq + 1 < sb.n && item_in >= sb.item_off[sq + 1]) ++sq;
+      item = item_in - sb.item_off[sq];
+      nb = sb.nb[sq];
+      L = sb.L[sq];
+      const size_t tok = (size_t)sb.tok_off[sq];
+      q = q_all + tok * Hq * D;
+      k = k_all + tok * Hkv * D;
+      out = out_all + tok * Hq * D;
+      vt = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(vt_all) + sb.vt_off[sq]);
+      row_count = rc_all + sb.rc_off[sq];
+      col_idx = ci_all + sb.ci_off[sq];
+      const int Gs = Hq / Hkv;
+      const int own = Gs % 2 ? Hkv * ((nb + 1) / 2) * Gs : Hkv * nb * (Gs / 2);
+      if (item >= own) return;  // padding up to the next range (uniform, before any barrier)
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     C cx;
@@ -1137,10 +1190,31 @@ hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_
   const dim3 grid((unsigned)(g.Hkv * g.nb));
   const __bf16* vv = static_cast<const __bf16*>(v);
   __bf16* out = static_cast<__bf16*>(vt);
-  if (g.d == 128 && g.B == 128) transpose_v_kernel<128, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
-  else if (g.d == 128 && g.B == 64) transpose_v_kernel<128, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
-  else if (g.d == 64 && g.B == 128) transpose_v_kernel<64, 128><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
-  else transpose_v_kernel<64, 64><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues);
+  const NoBatch nob{};
+#define RR_TV(DV, BV) transpose_v_kernel<DV, BV, false><<<grid, 256, 0, st>>>(vv, out, g.Hkv, g.nb, g.L, queues, nob)
+  if (g.d == 128 && g.B == 128) RR_TV(128, 128);
+  else if (g.d == 128 && g.B == 64) RR_TV(128, 64);
+  else if (g.d == 64 && g.B == 128) RR_TV(64, 128);
+  else RR_TV(64, 64);
+#undef RR_TV
+  return hipGetLastError();
+}
+
+bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128 && g.Hq / g.Hkv >= 2; }
+
+int attn_items(const Geometry& g) {
+  const int G = g.Hq / g.Hkv;
+  return G % 2 ? g.Hkv * ((g.nb + 1) / 2) * G : g.Hkv * g.nb * (G / 2);
+}
+
+hipError_t launch_transpose_v_batched(const Geometry& g, const SeqBatch& sb, const void* v, void* vt,
+                                      int32_t* queues, hipStream_t st) {
+  if (!attn_pair_shape(g) || sb.n < 1 || sb.n > kMaxSeqPerLaunch) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)sb.tile_off[sb.n]);
+  const __bf16* vv = static_cast<const __bf16*>(v);
+  __bf16* out = static_cast<__bf16*>(vt);
+  if (g.d == 128) transpose_v_kernel<128, 128, true><<<grid, 256, 0, st>>>(vv, out, g.Hkv, 0, 0, queues, sb);
+  else transpose_v_kernel<64, 128, true><<<grid, 256, 0, st>>>(vv, out, g.Hkv, 0, 0, queues, sb);
   return hipGetLastError();
 }
 
@@ -1177,9 +1251,11 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
       if (e != hipSuccess) return e;
       const int two = nq == kAttnQueues && nitems > 16 * ncu ? 1 : 0;
       const dim3 fgrid((unsigned)nitems);
-#define RR_PP_LAUNCH(DV, ODD)                                                                      \
-  attn_bf16_pp_kernel<DV, 128, ODD><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
-                                                           g.nb, g.causal, cscale, g.L, queues, nq, nitems, two)
+      const NoBatch nob{};
+#define RR_PP_LAUNCH(DV, ODD)                                                                             \
+  attn_bf16_pp_kernel<DV, 128, ODD, false><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
+                                                                  g.nb, g.causal, cscale, g.L, queues, nq, nitems, two, \
+                                                                  nob)
       if (g.d == 128) {
         if (G % 2) RR_PP_LAUNCH(128, true); else RR_PP_LAUNCH(128, false);
       } else {
@@ -1218,6 +1294,40 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
   RR_F32_CASE(64, 64)
 #undef RR_F32_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_batched(const Geometry& g, const SeqBatch& sb, const void* q, const void* k,
+                                    const void* vt, int32_t* queues, const int32_t* row_count,
+                                    const int32_t* col_idx, void* out, hipStream_t st) {
+  if (!attn_pair_shape(g) || sb.n < 1 || sb.n > kMaxSeqPerLaunch) return hipErrorInvalidValue;
+  const float cscale = (1.0f / sqrtf((float)g.d)) * 1.4426950408889634f;
+  const int G = g.Hq / g.Hkv;
+  const int nitems = sb.item_off[sb.n];  // a multiple of 16: every range starts on one
+  int ncu = 0;
+  const hipError_t e = stream_cu_count(st, &ncu);
+  if (e != hipSuccess) return e;
+  // One item per workgroup in launch order: claiming two items per workgroup
+  // from the per-XCD queues (as the single-sequence launch does at 128K-class
+  // sizes) made the eight-sequence 128K-token batch 6% slower, the static
+  // order 1% faster than one launch per sequence.
+  (void)ncu;
+  const int two = 0;
+  const dim3 fgrid((unsigned)nitems);
+  const __bf16* qq = static_cast<const __bf16*>(q);
+  const __bf16* kk = static_cast<const __bf16*>(k);
+  const __bf16* vv = static_cast<const __bf16*>(vt);
+  __bf16* oo = static_cast<__bf16*>(out);
+#define RR_PPB_LAUNCH(DV, ODD)                                                                            \
+  attn_bf16_pp_kernel<DV, 128, ODD, true><<<fgrid, 512, 0, st>>>(qq, kk, vv, row_count, col_idx, oo, g.Hq, g.Hkv, \
+                                                                 0, g.causal, cscale, 0, queues, kAttnQueues, nitems, \
+                                                                 two, sb)
+  if (g.d == 128) {
+    if (G % 2) RR_PPB_LAUNCH(128, true); else RR_PPB_LAUNCH(128, false);
+  } else {
+    if (G % 2) RR_PPB_LAUNCH(64, true); else RR_PPB_LAUNCH(64, false);
+  }
+#undef RR_PPB_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace rr

@@ -8,6 +8,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <new>
+
 #include "rr_attn.h"
 #include "rr_kernels.h"
 
@@ -59,6 +62,9 @@ struct Workspace {
   size_t kbar, mass, vt, queues, total;  // byte offsets and total size
 };
 
+// V re-laid out per key block (bf16 attention kernels)
+size_t vt_bytes(const rr::Geometry& g) { return (size_t)g.nb * g.B * g.Hkv * g.d * 2; }
+
 Workspace layout(const rr::Geometry& g) {
   const size_t esz = g.bf16 ? 2 : 4;
   Workspace w;
@@ -68,7 +74,7 @@ Workspace layout(const rr::Geometry& g) {
   w.mass = off;
   off += align_up((size_t)g.Hq * g.nb * g.nb * sizeof(float));
   w.vt = off;  // nb whole tiles: a short last block is padded with zeros
-  if (g.bf16) off += align_up((size_t)g.nb * g.B * g.Hkv * g.d * esz);
+  if (g.bf16) off += align_up(vt_bytes(g));
   w.queues = off;  // the attention's work-queue counters
   if (g.bf16) off += align_up(rr::kAttnQueues * sizeof(int32_t));
   w.total = off;
@@ -176,12 +182,23 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
 }
 
 // Packed variable-length batch: the per-sequence problems, validated before
-// anything is enqueued.
+// anything is enqueued, and the workspace the batch needs. Every search runs
+// on the first part (pooled keys and masses of the longest sequence). With
+// the head-pair kernel the attention of the whole batch is one launch, so
+// every sequence's V re-layout follows (vt_base, in sequence order), then the
+// queue counters (queues); otherwise each sequence's attention reuses the
+// workspace as a single sequence would.
+struct VarlenWorkspace {
+  size_t vt_base, queues, total;
+  bool batched;
+};
+
 static rr_status varlen_geometries(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens,
-                                   size_t* ws_max) {
+                                   VarlenWorkspace* vw) {
   if (!p || n_seq <= 0 || !seq_lens) return RR_ERR_INVALID_ARG;
   long long total = 0;
-  size_t need = 0;
+  size_t single = 0, search = 0, vts = 0;
+  bool pair = false;
   for (int32_t b = 0; b < n_seq; ++b) {
     if (seq_lens[b] <= 0) return RR_ERR_INVALID_ARG;
     rr_problem pb = *p;
@@ -189,26 +206,33 @@ static rr_status varlen_geometries(const rr_problem* p, int32_t n_seq, const int
     rr::Geometry g;
     const rr_status s = make_geometry(&pb, &g);
     if (s != RR_OK) return s;
-    const size_t w = layout(g).total;
-    if (w > need) need = w;
+    const Workspace w = layout(g);
+    single = std::max(single, w.total);
+    search = std::max(search, w.vt);  // pooled keys and masses
+    vts += align_up(vt_bytes(g));
+    pair = rr::attn_pair_shape(g);
     total += seq_lens[b];
   }
   if (total != p->L) return RR_ERR_INVALID_ARG;
-  *ws_max = need;
+  vw->batched = pair;
+  vw->vt_base = search;
+  vw->queues = search + vts;
+  vw->total = pair ? vw->queues + align_up(rr::kAttnQueues * sizeof(int32_t)) : single;
   return RR_OK;
 }
 
 size_t rr_workspace_bytes_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens) {
-  size_t need = 0;
-  return varlen_geometries(p, n_seq, seq_lens, &need) == RR_OK ? need : 0;
+  VarlenWorkspace vw;
+  return varlen_geometries(p, n_seq, seq_lens, &vw) == RR_OK ? vw.total : 0;
 }
 
 rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens, const void* q,
                             const void* k, const void* v, void* out, int32_t* row_count, int32_t* col_idx,
                             void* ws, size_t ws_bytes, void* stream) {
-  size_t need = 0;
-  rr_status s = varlen_geometries(p, n_seq, seq_lens, &need);
+  VarlenWorkspace vw;
+  rr_status s = varlen_geometries(p, n_seq, seq_lens, &vw);
   if (s != RR_OK) return s;
+  const size_t need = vw.total;
   if (!q || !k || !v || !out || !row_count || !col_idx) return RR_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(row_count) ||
       !aligned16(col_idx))
@@ -222,6 +246,8 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
       return RR_ERR_UNSUPPORTED;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // the search of each sequence, one after the other (they share the
+  // workspace's pooled-key and mass regions)
   size_t tok = 0, rc_off = 0, ci_off = 0;
   for (int32_t b = 0; b < n_seq; ++b) {
     rr_problem pb = *p;
@@ -230,19 +256,91 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
     make_geometry(&pb, &g);
     const uint8_t* qb = static_cast<const uint8_t*>(q) + tok * p->Hq * p->d * esz;
     const uint8_t* kb = static_cast<const uint8_t*>(k) + tok * p->Hkv * p->d * esz;
-    const uint8_t* vb = static_cast<const uint8_t*>(v) + tok * p->Hkv * p->d * esz;
-    uint8_t* ob = static_cast<uint8_t*>(out) + tok * p->Hq * p->d * esz;
-    int32_t* rcb = row_count + rc_off;
-    int32_t* cib = col_idx + ci_off;
-    s = run_search(g, qb, kb, rcb, cib, nullptr, nullptr, ws, st);
-    if (s != RR_OK) return s;
-    s = run_attention(g, qb, kb, vb, rcb, cib, ob, ws, st);
+    s = run_search(g, qb, kb, row_count + rc_off, col_idx + ci_off, nullptr, nullptr, ws, st);
     if (s != RR_OK) return s;
     tok += seq_lens[b];
     rc_off += (size_t)g.Hq * g.nb;
     ci_off += (size_t)g.Hq * g.nb * g.nb;
   }
-  return RR_OK;
+  rr_problem p0 = *p;
+  p0.L = seq_lens[0];
+  rr::Geometry g0;
+  make_geometry(&p0, &g0);
+  if (!vw.batched) {  // the other kernels: one attention launch per sequence
+    tok = rc_off = ci_off = 0;
+    for (int32_t b = 0; b < n_seq; ++b) {
+      rr_problem pb = *p;
+      pb.L = seq_lens[b];
+      rr::Geometry g;
+      make_geometry(&pb, &g);
+      const uint8_t* qb = static_cast<const uint8_t*>(q) + tok * p->Hq * p->d * esz;
+      const uint8_t* kb = static_cast<const uint8_t*>(k) + tok * p->Hkv * p->d * esz;
+      const uint8_t* vb = static_cast<const uint8_t*>(v) + tok * p->Hkv * p->d * esz;
+      uint8_t* ob = static_cast<uint8_t*>(out) + tok * p->Hq * p->d * esz;
+      s = run_attention(g, qb, kb, vb, row_count + rc_off, col_idx + ci_off, ob, ws, st);
+      if (s != RR_OK) return s;
+      tok += seq_lens[b];
+      rc_off += (size_t)g.Hq * g.nb;
+      ci_off += (size_t)g.Hq * g.nb * g.nb;
+    }
+    return RR_OK;
+  }
+  // The head-pair attention of every sequence in one launch (per group of
+  // kMaxSeqPerLaunch), after one V re-layout launch for the group: longest
+  // sequences first, so the launch starts with the longest rows, each
+  // sequence's work items on a range of their own.
+  struct Seq {
+    int32_t len;
+    size_t tok, rc, ci, vt;
+  };
+  Seq seqs_small[64];
+  Seq* seqs = n_seq <= 64 ? seqs_small : new (std::nothrow) Seq[n_seq];
+  if (!seqs) return RR_ERR_INVALID_ARG;
+  tok = rc_off = ci_off = 0;
+  size_t vt_off = 0;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    rr_problem pb = *p;
+    pb.L = seq_lens[b];
+    rr::Geometry g;
+    make_geometry(&pb, &g);
+    seqs[b] = Seq{seq_lens[b], tok, rc_off, ci_off, vt_off};
+    tok += seq_lens[b];
+    rc_off += (size_t)g.Hq * g.nb;
+    ci_off += (size_t)g.Hq * g.nb * g.nb;
+    vt_off += align_up(vt_bytes(g));
+  }
+  std::stable_sort(seqs, seqs + n_seq, [](const Seq& a, const Seq& b) { return a.len > b.len; });
+  uint8_t* vt = static_cast<uint8_t*>(ws) + vw.vt_base;
+  int32_t* queues = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + vw.queues);
+  hipError_t e = hipSuccess;
+  for (int32_t b0 = 0; b0 < n_seq && e == hipSuccess; b0 += rr::kMaxSeqPerLaunch) {
+    rr::SeqBatch sb;
+    sb.n = std::min<int32_t>(rr::kMaxSeqPerLaunch, n_seq - b0);
+    int items = 0, tiles = 0;
+    for (int m = 0; m < sb.n; ++m) {
+      const Seq& sq = seqs[b0 + m];
+      rr_problem pb = *p;
+      pb.L = sq.len;
+      rr::Geometry g;
+      make_geometry(&pb, &g);
+      sb.item_off[m] = items;
+      sb.tile_off[m] = tiles;
+      sb.tok_off[m] = (int)sq.tok;
+      sb.L[m] = sq.len;
+      sb.nb[m] = g.nb;
+      sb.rc_off[m] = (long long)sq.rc;
+      sb.ci_off[m] = (long long)sq.ci;
+      sb.vt_off[m] = (long long)sq.vt;
+      items += (rr::attn_items(g) + 15) / 16 * 16;
+      tiles += g.Hkv * g.nb;
+    }
+    sb.item_off[sb.n] = items;
+    sb.tile_off[sb.n] = tiles;
+    e = rr::launch_transpose_v_batched(g0, sb, v, vt, queues, st);
+    if (e == hipSuccess) e = rr::launch_attention_batched(g0, sb, q, k, vt, queues, row_count, col_idx, out, st);
+  }
+  if (seqs != seqs_small) delete[] seqs;
+  return hip_status(e);
 }
 
 rr_status rr_mass_recall(const rr_problem* p, const void* q, const void* k, const int32_t* row_count,

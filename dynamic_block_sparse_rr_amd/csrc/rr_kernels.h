@@ -31,14 +31,42 @@ hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, in
 hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,
                               int32_t* out_count, int32_t* out_idx, hipStream_t st);
 
+// A packed batch of sequences covered by one launch of the head-pair
+// attention and one of its V re-layout: per sequence its first token, length,
+// block count, the entry offsets of its block lists, the byte offset of its V
+// re-layout, the first of its work items (multiples of 16; item_off[n] is the
+// total) and the first of its V tiles (tile_off[n] is the total).
+constexpr int kMaxSeqPerLaunch = 32;
+struct SeqBatch {
+  int n;
+  int item_off[kMaxSeqPerLaunch + 1];
+  int tile_off[kMaxSeqPerLaunch + 1];
+  int tok_off[kMaxSeqPerLaunch];
+  int L[kMaxSeqPerLaunch];
+  int nb[kMaxSeqPerLaunch];
+  long long rc_off[kMaxSeqPerLaunch];
+  long long ci_off[kMaxSeqPerLaunch];
+  long long vt_off[kMaxSeqPerLaunch];
+};
+
 // Stage 2 launches. queues: kAttnQueues device counters of the bf16
 // attention's work queues (one per XCD); launch_transpose_v zeroes them, so
 // the two run in this order on one stream, one pair per call at a time.
 constexpr int kAttnQueues = 8;
+bool attn_pair_shape(const Geometry& g);  // bf16, B = 128, two or more query heads per KV head
+int attn_items(const Geometry& g);        // work items of one sequence's head-pair launch
 hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_t* queues, hipStream_t st);
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const void* vt, int32_t* queues, const int32_t* row_count,
                             const int32_t* col_idx, void* out, hipStream_t st);
+// The batched head-pair forms: g describes the sequences but for L and nb
+// (taken from sb); q, k, v, out are the packed tensors, row_count / col_idx
+// the packed lists, vt the base of the sequences' re-layouts.
+hipError_t launch_transpose_v_batched(const Geometry& g, const SeqBatch& sb, const void* v, void* vt,
+                                      int32_t* queues, hipStream_t st);
+hipError_t launch_attention_batched(const Geometry& g, const SeqBatch& sb, const void* q, const void* k,
+                                    const void* vt, int32_t* queues, const int32_t* row_count,
+                                    const int32_t* col_idx, void* out, hipStream_t st);
 
 // Selection quality: full-attention softmax mass inside the selected blocks.
 hipError_t launch_recall(const Geometry& g, const void* q, const void* k, const int32_t* row_count,
@@ -67,6 +95,6 @@ constexpr size_t kStaticWorkspaceBytes = 32u << 20;
 hipError_t static_workspace(hipStream_t st, void** ptr);
 
 // Kernel-side limits checked by the host before any launch.
-constexpr int kMaxSelectBlocks = 8192;  // LDS sort capacity of the select kernel (nb): 12 B per key
+constexpr int kMaxSelectBlocks = 8192;  // block rows the select kernel stages in LDS: 4 rows x nb floats per workgroup
 
 }  // namespace rr

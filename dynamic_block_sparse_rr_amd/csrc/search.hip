@@ -25,10 +25,10 @@
 //               theirs through LDS in a fixed order; pass 2 recomputes the
 //               scores, forms probabilities and reduces them into key-block
 //               masses with a fixed shuffle tree (deterministic, no atomics).
-//   select      one workgroup per (h, i): bitonic sort of (mass desc, index asc)
-//               keys in LDS, prefix sums of the sorted masses, cut at the first
-//               block whose preceding mass reaches tau * total, and compaction
-//               of the kept blocks into an ascending list.
+//   select      one wave per (h, i): the Top-tau cut of the (mass desc, index
+//               asc) order found without sorting, by bisection on the bits of
+//               the cut mass (see the kernel), then the kept blocks compacted
+//               into an ascending list.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -131,11 +131,38 @@ __device__ __forceinline__ void merge_max_sum(float& m, float& l, float m2, floa
   m = mm;
 }
 
+// Cross-lane sums without LDS round trips (DPP and permlane moves). Every
+// step adds two equal-sized partial sums, so all lanes of a group end with
+// the same value (float addition commutes), the value an xor butterfly over
+// the same lanes gives.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// x + the value of the lane 32 apart
+__device__ __forceinline__ float add_halves(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+// sum over aligned groups of N consecutive lanes (N a power of two <= 32)
+template <int N>
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror: the other 8 of the 16
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
 // Lane layout of one 32x32 MFMA output (rows = key strides, cols = sampled
 // queries): lane owns column (lane & 31) and rows 8*(v/4) + 4*(lane/32) + v%4.
 __device__ __forceinline__ int out_row(int v, int half) { return 8 * (v >> 2) + 4 * half + (v & 3); }
 
-template <typename T, int D, int R>
+// CT: column tiles of sampled queries the kernel can hold (1 when a
+// workgroup's heads times R fit in 32 columns, which keeps the registers of
+// the second tile free).
+template <typename T, int D, int R, int CT, bool PF = false>
 __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, const T* __restrict__ kbar,
                                                      float* __restrict__ mass, int Hq, int Hkv, int S,
                                                      int nb, int ns, int causal, int hpc, int nchunk,
@@ -157,15 +184,15 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
   const int h0 = g * G + chunk * hpc;
   const int nh = min(hpc, G - chunk * hpc);
   const int NQ = nh * R;
-  const int NCT = (NQ + 31) >> 5;  // 1 or 2 column tiles of sampled queries
+  const int NCT = min((NQ + 31) >> 5, CT);  // 1 or 2 column tiles of sampled queries
   const int tcnt = causal ? (i + 1) * R : ns;
   const int ntile = (tcnt + 31) >> 5;
 
   // sampled queries (MFMA B operand, kept in registers) and the last visible stride of each
-  chunk_t qf[2][NCH];
-  int lim[2];
+  chunk_t qf[CT][NCH];
+  int lim[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     const int qi = ct * 32 + n32;
     if (ct < NCT && qi < NQ) {
       const int hl = qi / R, a = qi % R;
@@ -186,22 +213,40 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
   // pooled keys in the chunk-major layout: chunk cc of stride t of KV head g
   // at (g * 2 * NCH + cc) * ns + t, so one operand load (32 strides, one chunk
   // per lane half) reads two contiguous 512-byte runs
+  // (read through a buffer descriptor over this KV head's pooled keys, so
+  // every load is a per-lane 32-bit offset plus a uniform one per chunk)
   const chunk_t* kcm = reinterpret_cast<const chunk_t*>(kbar) + (size_t)g * 2 * NCH * ns;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<chunk_t*>(kcm), 0, 2 * NCH * ns * 16, 0x00020000);
 
   // a tile all of whose strides every sampled query sees needs no mask (the
   // padding columns past NQ then hold values that are never written)
   const int lim_all = causal ? i * R : ns - 1;
 
   // ---- pass 1: running max / sum of exp2(scaled score) per sampled query
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.0f, 0.0f};
-  for (int tile = wave; tile < ntile; tile += 4) {
-    const int trow = min(tile * 32 + n32, ns - 1);
-    chunk_t kf[NCH];
+  float mrun[CT], lrun[CT];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
+  for (int ct = 0; ct < CT; ++ct) {
+    mrun[ct] = -INFINITY;
+    lrun[ct] = 0.0f;
+  }
+  // pooled-key operands of tile `tile` (one 16-byte chunk per lane and k-step);
+  // the next tile's are loaded while this one is computed (PF: prefetch)
+  auto load_tile = [&](chunk_t (&kf)[NCH], int tile) __attribute__((always_inline)) {
+    const int trow = min(tile * 32 + n32, ns - 1);
+    const int voff = (half * ns + trow) * 16;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      kf[c] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 2 * c * ns * 16, 0));
+  };
+  chunk_t kf[NCH], kn[NCH];
+  if (wave < ntile) load_tile(kf, wave);
+  for (int tile = wave; tile < ntile; tile += 4) {
+    if (PF && tile + 4 < ntile) load_tile(kn, tile + 4);
+    if (!PF) load_tile(kf, tile);
     const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if (ct >= NCT) break;
       f32x16 acc = {};
 #pragma unroll
@@ -228,12 +273,16 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
         mrun[ct] = mnew;
       }
     }
+    if (PF) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) kf[c] = kn[c];
+    }
   }
 
   // merge the two lane halves, then the four waves (fixed order)
   __shared__ float sm_m[4][64], sm_l[4][64];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     const float mo = __shfl_xor(mrun[ct], 32);
     const float lo = __shfl_xor(lrun[ct], 32);
     merge_max_sum(mrun[ct], lrun[ct], mo, lo);
@@ -243,9 +292,9 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     }
   }
   __syncthreads();
-  float mu[2], invl[2];
+  float mu[CT], invl[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     float m = sm_m[0][ct * 32 + n32], l = sm_l[0][ct * 32 + n32];
 #pragma unroll
     for (int w = 1; w < 4; ++w) merge_max_sum(m, l, sm_m[w][ct * 32 + n32], sm_l[w][ct * 32 + n32]);
@@ -255,14 +304,13 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
 
   // ---- pass 2: probabilities summed into key blocks of R strides
   const float invR = 1.0f / (float)R;  // exact
+  if (wave < ntile) load_tile(kf, wave);
   for (int tile = wave; tile < ntile; tile += 4) {
-    const int trow = min(tile * 32 + n32, ns - 1);
-    chunk_t kf[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) kf[c] = kcm[(size_t)(2 * c + half) * ns + trow];
+    if (PF && tile + 4 < ntile) load_tile(kn, tile + 4);
+    if (!PF) load_tile(kf, tile);
     const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if (ct >= NCT) break;
       f32x16 acc = {};
 #pragma unroll
@@ -304,14 +352,11 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
       for (int k = 0; k < NW; ++k) w[k] *= invl[ct];
       if constexpr (R >= 8) {
 #pragma unroll
-        for (int k = 0; k < NW; ++k) w[k] += __shfl_xor(w[k], 32);
+        for (int k = 0; k < NW; ++k) w[k] = add_halves(w[k]);
       }
       // sum over the R sampled queries of the head (R consecutive lanes)
 #pragma unroll
-      for (int off = 1; off < R; off <<= 1) {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) w[k] += __shfl_xor(w[k], off);
-      }
+      for (int k = 0; k < NW; ++k) w[k] = sum_lane_groups<R>(w[k]);
       const int qi = ct * 32 + n32;
       const int hl = qi / R;
       const bool writer = (qi % R == 0) && hl < nh && (R < 8 || half == 0);
@@ -328,21 +373,54 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
         }
       }
     }
+    if (PF) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) kf[c] = kn[c];
+    }
   }
 }
 
 // ------------------------------------------------------------------ selection
 
+// Sum over the 64 lanes in one fixed order (xor butterfly), taken from lane 0
+// so every lane holds the same value.
+__device__ __forceinline__ float wave_total(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
+// Bits of a non-negative mass, ordered like its value (anything else reads as 0).
+__device__ __forceinline__ uint32_t mass_bits(float m) { return m > 0.0f ? __float_as_uint(m) : 0u; }
+
+// Top-tau cut of one row per wave (four rows per workgroup, no workgroup
+// barriers). The row's candidate masses are staged in LDS. In the (mass
+// descending, index ascending) order, block k is kept while the mass before
+// it is < tau * total; equivalently, with theta the largest mass value v such
+// that the masses >= v reach tau * total (found by bisection on the bits of
+// v, each step one sum over the row): every block heavier than theta is
+// kept, no lighter one is, and the blocks of mass exactly theta are kept in
+// index order while S(> theta) + (equal ones before) * theta < tau * total.
+// Sums run in one fixed order, so the cut is deterministic; it can differ from
+// a sequential prefix sum only where the cumulative mass lies within float
+// rounding of the threshold. At least one block is kept (the first of the
+// order: the heaviest, lowest index) even when every mass is zero. The kept
+// blocks are written in ascending order (ballot and prefix count per 64).
 __global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, int zero_fill,
                                                      int32_t* __restrict__ row_count,
-                                                     int32_t* __restrict__ col_idx, int nb, int causal,
+                                                     int32_t* __restrict__ col_idx, int nrows, int nb, int causal,
                                                      float tau_all, const float* __restrict__ tau_heads) {
-  extern __shared__ uint64_t keys[];  // np2 sort keys, then np2 int flags
-  __shared__ float part[256];
-  __shared__ int ipart[256];
-  __shared__ int cut;
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x;
+  extern __shared__ float srow_all[];  // one row of nb masses per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= nrows) return;  // the whole wave; nothing below waits for the other waves
+  float* srow = srow_all + wave * nb;
   const int i = row % nb;
   const int ncand = causal ? i + 1 : nb;
   float* mrow = mass + (size_t)row * nb;
@@ -354,85 +432,60 @@ __global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, i
 
   if (zero_fill) {  // exported masses: non-candidates and the unsearched last row are zero
     const int from = (i == nb - 1) ? 0 : ncand;
-    for (int j = from + tid; j < nb; j += 256) mrow[j] = 0.0f;
+    for (int j = from + lane; j < nb; j += 64) mrow[j] = 0.0f;
   }
   if (i == nb - 1 || tau >= 1.0f) {  // static last-block protection / tau = 1
-    for (int j = tid; j < ncand; j += 256) out[j] = j;
-    if (tid == 0) row_count[row] = ncand;
+    for (int j = lane; j < ncand; j += 64) out[j] = j;
+    if (lane == 0) row_count[row] = ncand;
     return;
   }
 
-  int np2 = 1;
-  while (np2 < ncand) np2 <<= 1;
-  int* flags = reinterpret_cast<int*>(keys + np2);
-  for (int j = tid; j < np2; j += 256) {
-    keys[j] = (j < ncand) ? (((uint64_t)(~__float_as_uint(mrow[j])) << 32) | (uint32_t)j) : ~0ull;
-    flags[j] = 0;
+  float part = 0.0f, mx = 0.0f;
+  for (int j = lane; j < ncand; j += 64) {
+    const float m = mrow[j];
+    srow[j] = m;
+    part += m;
+    mx = fmaxf(mx, m);
   }
-  if (tid == 0) cut = ncand;
-  __syncthreads();
-
-  // bitonic sort, ascending key = mass descending, block index ascending
-  for (int kk = 2; kk <= np2; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int idx = tid; idx < (np2 >> 1); idx += 256) {
-        const int a = 2 * idx - (idx & (jj - 1));
-        const int b = a + jj;
-        const uint64_t ka = keys[a], kb = keys[b];
-        const bool up = (a & kk) == 0;
-        if ((ka > kb) == up) {
-          keys[a] = kb;
-          keys[b] = ka;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // prefix sums of the sorted masses: per-thread segments + a fixed-order scan
-  const int seg = (np2 + 255) / 256;
-  const int lo = tid * seg, hi = min(lo + seg, ncand);
-  float s = 0.0f;
-  for (int k = lo; k < hi; ++k) s += __uint_as_float(~(uint32_t)(keys[k] >> 32));
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const float add = (tid >= off) ? part[tid - off] : 0.0f;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  const float total = part[255];
+  const float total = wave_total(part);
+  const uint32_t vmax = mass_bits(wave_max(mx));
   const float thr = tau * total;
-  float before = (tid == 0) ? 0.0f : part[tid - 1];
-  for (int k = lo; k < hi; ++k) {
-    if (!(before < thr)) {
-      atomicMin(&cut, k);
-      break;
+  // theta: the largest v <= the maximum mass with S(>= v) >= thr
+  uint32_t v = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = v | (1u << bit);
+    if (cand > vmax) continue;  // uniform
+    float sp = 0.0f;
+    for (int j = lane; j < ncand; j += 64) {
+      const float m = srow[j];
+      sp += mass_bits(m) >= cand ? m : 0.0f;
     }
-    before += __uint_as_float(~(uint32_t)(keys[k] >> 32));
+    if (wave_total(sp) >= thr) v = cand;
   }
-  __syncthreads();
-  const int kept = max(cut, 1);
-  for (int k = tid; k < kept; k += 256) flags[(uint32_t)keys[k]] = 1;
-  __syncthreads();
-
-  // compaction in ascending block order
-  int c = 0;
-  const int jlo = tid * seg, jhi = min(jlo + seg, ncand);
-  for (int j = jlo; j < jhi; ++j) c += flags[j];
-  ipart[tid] = c;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = (tid >= off) ? ipart[tid - off] : 0;
-    __syncthreads();
-    ipart[tid] += add;
-    __syncthreads();
+  float gp = 0.0f;
+  for (int j = lane; j < ncand; j += 64) {
+    const float m = srow[j];
+    gp += mass_bits(m) > v ? m : 0.0f;
   }
-  int pos = (tid == 0) ? 0 : ipart[tid - 1];
-  for (int j = jlo; j < jhi; ++j)
-    if (flags[j]) out[pos++] = j;
-  if (tid == 0) row_count[row] = ipart[255];
+  const float sgt = wave_total(gp);  // S(> theta)
+  const float theta = __uint_as_float(v);
+  int base = 0, eq_before = 0;
+  for (int j0 = 0; j0 < ncand; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t bj = j < ncand ? mass_bits(srow[j]) : 0u;
+    const bool eq = j < ncand && bj == v;
+    const uint64_t eqmask = __ballot(eq);
+    const int c = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eqmask >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)eqmask, 0u));
+    const bool keep = j < ncand && (bj > v || (eq && (sgt + (float)c * theta < thr || (c == 0 && sgt == 0.0f))));
+    const uint64_t kmask = __ballot(keep);
+    const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(kmask >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)kmask, 0u));
+    if (keep) out[pos] = j;
+    base += __popcll(kmask);
+    eq_before += __popcll(eqmask);
+  }
+  if (lane == 0) row_count[row] = base;
 }
 
 // Shared mask per KV head (a variant of the per-head masks, not on the pages:
@@ -739,10 +792,15 @@ hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, f
   const float cscale = (1.0f / sqrtf((float)g.d)) * 1.4426950408889634f;
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(kbar);
-#define RR_SEARCH_CASE(RV)                                                                      \
-  case RV:                                                                                      \
-    search_kernel<T, D, RV><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns,   \
-                                                  g.causal, hpc, nchunk, cscale);              \
+  const bool one_tile = hpc * g.r <= 32;
+#define RR_SEARCH_CASE(RV)                                                                        \
+  case RV:                                                                                        \
+    if (one_tile)                                                                                 \
+      search_kernel<T, D, RV, 1><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
+                                                       g.causal, hpc, nchunk, cscale);           \
+    else                                                                                          \
+      search_kernel<T, D, RV, 2><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
+                                                       g.causal, hpc, nchunk, cscale);           \
     break;
   switch (g.r) {
     RR_SEARCH_CASE(2)
@@ -788,15 +846,14 @@ hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, flo
 
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
                          int32_t* col_idx, const float* tau_heads, hipStream_t st) {
-  int np2 = 1;
-  while (np2 < g.nb) np2 <<= 1;
-  const size_t lds = (size_t)np2 * (sizeof(uint64_t) + sizeof(int));
+  const size_t lds = 4 * (size_t)g.nb * sizeof(float);  // one row per wave
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  select_kernel<<<dim3((unsigned)(g.Hq * g.nb)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill,
-                                                                 row_count, col_idx, g.nb, g.causal,
-                                                                 g.tau, tau_heads);
+  const int nrows = g.Hq * g.nb;
+  select_kernel<<<dim3((unsigned)((nrows + 3) / 4)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill, row_count,
+                                                                      col_idx, nrows, g.nb, g.causal, g.tau,
+                                                                      tau_heads);
   return hipGetLastError();
 }
 

@@ -106,17 +106,19 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  * ascending, < nb, and (causal) <= its query block index: rows breaking this
  * give undefined output (the library does not read lists back to the host).
  *   q, k, v     device inputs in p->dtype; out: device output [L][Hq][d] in p->dtype.
- *   ws          device workspace (bf16: holds a copy of V re-laid out as one
- *               channels-by-keys tile per key block, and the counters of the
- *               attention's work queues; calls that overlap in time need
- *               workspaces of their own).
+ *   ws          device workspace of rr_workspace_bytes(p) bytes (bf16: a
+ *               copy of V re-laid out as one channels-by-keys tile per key
+ *               block, and the counters of the attention's work queues; fp32
+ *               needs none of it); calls that overlap in time need
+ *               workspaces of their own.
  * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
  * p->S and p->tau are not used but must be valid.
  * The kernel is chosen from the problem alone: bf16 with B = 128 and two or
  * more query heads per KV head runs two query heads per workgroup in a
  * ping-pong schedule (with an odd count the last head of every KV head is
  * paired with itself over two adjacent query blocks in the same launch);
- * other bf16 shapes run one query head per workgroup.
+ * other bf16 shapes run one query head per workgroup; fp32 runs on the fp32
+ * matrix cores.
  */
 rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
                                const int32_t* row_count, const int32_t* col_idx, void* out,
@@ -182,9 +184,13 @@ rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, co
  * of sequence b follow those of the sequences before it: row_count at entry
  * offset sum_{b'<b} Hq nb_b', col_idx at sum_{b'<b} Hq nb_b'^2, with
  * nb_b = ceil(L_b / B). Every sequence's slices must stay 16-byte aligned
- * (else RR_ERR_UNSUPPORTED). The sequences run one after the other on the
- * stream, sharing one workspace of rr_workspace_bytes_varlen bytes (0 for an
- * invalid batch). All lengths are checked before anything is enqueued.
+ * (else RR_ERR_UNSUPPORTED). The searches run one after the other on the
+ * stream; the attention of the whole batch is one launch (per 32 sequences)
+ * where the problem has the head-pair kernel (bf16, B = 128, two or more
+ * query heads per KV head), longest sequences first, else one launch per
+ * sequence. One workspace of rr_workspace_bytes_varlen bytes serves them all
+ * (0 for an invalid batch). All lengths are checked before anything is
+ * enqueued.
  */
 size_t rr_workspace_bytes_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens);
 rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* seq_lens, const void* q,

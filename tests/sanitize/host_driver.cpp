@@ -108,6 +108,36 @@ int main() {
   void* vws = workspace(vneed);
   EXPECT(rr_prefill_varlen(&pv, 3, lens, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), vws, vneed, nullptr),
          RR_OK);
+  if (g_stub.batched_launches != 1) {  // three sequences: one head-pair launch
+    fprintf(stderr, "varlen attention: %ld batched launches\n", g_stub.batched_launches);
+    bad = 1;
+  }
+  free(vws);
+  {  // 40 sequences: two launch groups (32 + 8)
+    int32_t many[40];
+    int total = 0;
+    for (int b = 0; b < 40; ++b) total += (many[b] = 50 + 37 * b);
+    rr_problem pm = {total, 8, 2, 64, 8, 128, 0.9f, 1, RR_BF16};
+    const size_t mneed = rr_workspace_bytes_varlen(&pm, 40, many);
+    void* mws = workspace(mneed);
+    const long before_launches = g_stub.batched_launches;
+    EXPECT(rr_prefill_varlen(&pm, 40, many, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), mws, mneed,
+                             nullptr),
+           RR_OK);
+    if (g_stub.batched_launches - before_launches != 2) {
+      fprintf(stderr, "40 sequences: %ld batched launches\n", g_stub.batched_launches - before_launches);
+      bad = 1;
+    }
+    free(mws);
+    rr_problem pf = {300 + 1000 + 128, 4, 4, 64, 8, 64, 0.9f, 1, RR_FP32};  // per-sequence attention
+    const size_t fneed = rr_workspace_bytes_varlen(&pf, 3, lens);
+    void* fws = workspace(fneed);
+    EXPECT(rr_prefill_varlen(&pf, 3, lens, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), fws, fneed,
+                             nullptr),
+           RR_OK);
+    free(fws);
+    vws = workspace(vneed);
+  }
   const int32_t bad_lens[3] = {300, -5, 1133};
   EXPECT(rr_prefill_varlen(&pv, 3, bad_lens, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), vws, vneed,
                            nullptr),

@@ -54,6 +54,13 @@ hipError_t launch_union_lists(const Geometry&, const int32_t*, const int32_t*, i
   return hipSuccess;
 }
 
+bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128 && g.Hq / g.Hkv >= 2; }
+
+int attn_items(const Geometry& g) {
+  const int G = g.Hq / g.Hkv;
+  return G % 2 ? g.Hkv * ((g.nb + 1) / 2) * G : g.Hkv * g.nb * (G / 2);
+}
+
 hipError_t launch_transpose_v(const Geometry& g, const void*, void* vt, int32_t* queues, hipStream_t) {
   ++g_stub.calls;
   in_ws(vt, (size_t)g.nb * g.B * g.Hkv * g.d * esz(g), "V re-layout");
@@ -68,6 +75,38 @@ hipError_t launch_attention(const Geometry& g, const void*, const void*, const v
     in_ws(vt, (size_t)g.nb * g.B * g.Hkv * g.d * esz(g), "V re-layout (attention)");
     in_ws(queues, kAttnQueues * sizeof(int32_t), "work-queue counters (attention)");
   }
+  return hipSuccess;
+}
+
+static void check_batch(const Geometry& g, const SeqBatch& sb, const void* vt, int32_t* queues, bool tiles) {
+  if (!attn_pair_shape(g) || sb.n < 1 || sb.n > kMaxSeqPerLaunch) abort();
+  in_ws(queues, kAttnQueues * sizeof(int32_t), "work-queue counters (batched)");
+  for (int m = 0; m < sb.n; ++m) {  // ranges ascending and covering each sequence; longest first
+    Geometry gs = g;
+    gs.L = sb.L[m];
+    gs.nb = (sb.L[m] + g.B - 1) / g.B;
+    if (sb.nb[m] != gs.nb || sb.item_off[m] % 16 || sb.item_off[m + 1] - sb.item_off[m] < attn_items(gs)) abort();
+    if (tiles && sb.tile_off[m + 1] - sb.tile_off[m] != gs.Hkv * gs.nb) abort();
+    if (m > 0 && sb.L[m] > sb.L[m - 1]) abort();
+    in_ws(static_cast<const char*>(vt) + sb.vt_off[m], (size_t)gs.nb * gs.B * gs.Hkv * gs.d * esz(gs),
+          "V re-layout of one sequence (batched)");
+  }
+}
+
+hipError_t launch_transpose_v_batched(const Geometry& g, const SeqBatch& sb, const void*, void* vt, int32_t* queues,
+                                      hipStream_t) {
+  ++g_stub.calls;
+  check_batch(g, sb, vt, queues, true);
+  return hipSuccess;
+}
+
+hipError_t launch_attention_batched(const Geometry& g, const SeqBatch& sb, const void*, const void*,
+                                    const void* vt, int32_t* queues, const int32_t*, const int32_t*, void*,
+                                    hipStream_t) {
+  ++g_stub.calls;
+  check_batch(g, sb, vt, queues, false);
+  g_stub.batched_items += sb.item_off[sb.n];
+  ++g_stub.batched_launches;
   return hipSuccess;
 }
 

@@ -9,5 +9,7 @@ struct StubState {
   bool user_kbar = false;    // the caller passed its own pooled keys (decode)
   bool fail_launch = false;  // make the first launch report a failure
   long calls = 0;
+  long batched_launches = 0;  // head-pair attention launches over several sequences
+  long batched_items = 0;
 };
 extern StubState g_stub;
