@@ -162,7 +162,7 @@ __device__ __forceinline__ int out_row(int v, int half) { return 8 * (v >> 2) + 
 // CT: column tiles of sampled queries the kernel can hold (1 when a
 // workgroup's heads times R fit in 32 columns, which keeps the registers of
 // the second tile free).
-template <typename T, int D, int R, int CT, bool PF = false>
+template <typename T, int D, int R, int CT>
 __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, const T* __restrict__ kbar,
                                                      float* __restrict__ mass, int Hq, int Hkv, int S,
                                                      int nb, int ns, int causal, int hpc, int nchunk,
@@ -230,8 +230,9 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     mrun[ct] = -INFINITY;
     lrun[ct] = 0.0f;
   }
-  // pooled-key operands of tile `tile` (one 16-byte chunk per lane and k-step);
-  // the next tile's are loaded while this one is computed (PF: prefetch)
+  // pooled-key operands of tile `tile` (one 16-byte chunk per lane and k-step;
+  // loading the next tile's during this one's compute measured slower: the
+  // extra registers cost a wave per SIMD)
   auto load_tile = [&](chunk_t (&kf)[NCH], int tile) __attribute__((always_inline)) {
     const int trow = min(tile * 32 + n32, ns - 1);
     const int voff = (half * ns + trow) * 16;
@@ -239,11 +240,9 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
     for (int c = 0; c < NCH; ++c)
       kf[c] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 2 * c * ns * 16, 0));
   };
-  chunk_t kf[NCH], kn[NCH];
-  if (wave < ntile) load_tile(kf, wave);
+  chunk_t kf[NCH];
   for (int tile = wave; tile < ntile; tile += 4) {
-    if (PF && tile + 4 < ntile) load_tile(kn, tile + 4);
-    if (!PF) load_tile(kf, tile);
+    load_tile(kf, tile);
     const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -273,10 +272,6 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
         mrun[ct] = mnew;
       }
     }
-    if (PF) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) kf[c] = kn[c];
-    }
   }
 
   // merge the two lane halves, then the four waves (fixed order)
@@ -304,10 +299,8 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
 
   // ---- pass 2: probabilities summed into key blocks of R strides
   const float invR = 1.0f / (float)R;  // exact
-  if (wave < ntile) load_tile(kf, wave);
   for (int tile = wave; tile < ntile; tile += 4) {
-    if (PF && tile + 4 < ntile) load_tile(kn, tile + 4);
-    if (!PF) load_tile(kf, tile);
+    load_tile(kf, tile);
     const bool whole = tile * 32 + 31 <= lim_all;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -372,10 +365,6 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
           if (jb < nb && (!causal || jb <= i)) mrow[jb] = w[k] * invR;
         }
       }
-    }
-    if (PF) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) kf[c] = kn[c];
     }
   }
 }
