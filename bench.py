@@ -120,15 +120,18 @@ def cpu_baseline(w, q, k, v, rc, ci, f_comp, tau, n_attn_rows=8192, full=False):
     oracle.search(q, k, S=w.S, B=w.B, tau=tau, causal=w.causal, round_bf16=w.dtype == "bf16", extras=False)
     t_search = time.perf_counter() - t0
 
+    log("  oracle search %.2fs on %d threads" % (t_search, cores))
     if full and w.L > 32768:
         heads = [j * (w.Hq // 4) for j in range(4)]
-        rows = np.array([(x, h) for h in heads for x in range(w.L)], np.int32)
         f_sub = 0.0
-        for h in heads:
+        t_attn = 0.0
+        for h in heads:  # one head at a time, a progress line after each
             f_sub += computed_flops(rc[h:h + 1], ci[h:h + 1], w.B, w.d, w.causal)[0]
-        t0 = time.perf_counter()
-        oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=rows)
-        t_attn = time.perf_counter() - t0
+            rows = np.array([(x, h) for x in range(w.L)], np.int32)
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=rows)
+            t_attn += time.perf_counter() - t0
+            log("  oracle attention, head %d: %.1fs" % (h, t_attn))
         est = t_search + t_attn * (f_comp / f_sub)
         return {
             "value": f_comp / est / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -139,9 +142,14 @@ def cpu_baseline(w, q, k, v, rc, ci, f_comp, tau, n_attn_rows=8192, full=False):
             "search_s": round(t_search, 3), "attn_heads_s": round(t_attn, 3), "step_s_est": round(est, 1),
         }
     if full or w.L * w.Hq <= n_attn_rows:  # the whole attention, nothing extrapolated
-        t0 = time.perf_counter()
-        oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal)
-        t_attn = time.perf_counter() - t0
+        t_attn = 0.0
+        for h in range(w.Hq):  # one head at a time, a progress line after each
+            rows = np.array([(x, h) for x in range(w.L)], np.int32)
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, rc, ci, B=w.B, causal=w.causal, rows=rows)
+            t_attn += time.perf_counter() - t0
+            if w.L > 4096:
+                log("  oracle attention, head %d: %.1fs" % (h, t_attn))
         est = t_search + t_attn
         return {
             "value": f_comp / est / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -579,6 +587,17 @@ def main():
             ("32x32x16 bf16" if w.dtype == "bf16" else "32x32x2 fp32"))
         if w.dtype == "bf16":
             line["roofline"]["peak_lds_fed_measured"] = float(peaks["mfma_bf16_lds_2w_TFLOPs"])
+            # the same MFMA stream on pseudo-random operands: the rate the chip sustains when every
+            # multiplier bit toggles as in real activations (its clock drops under that load)
+            mr = float(peaks.get("mfma_bf16_reg_2w_random_TFLOPs", 0.0))
+            if mr > 0:
+                line["roofline"]["peak_measured_random_operands"] = mr
+                line["roofline"]["frac_measured_random_operands"] = round(attn_tflops / mr, 4)
+            # ... and fed like the attention: one LDS operand per MFMA, pseudo-random data
+            ml = float(peaks.get("mfma_bf16_lds_2w_random_TFLOPs", 0.0))
+            if ml > 0:
+                line["roofline"]["peak_lds_fed_random_operands"] = ml
+                line["roofline"]["frac_lds_fed_random_operands"] = round(attn_tflops / ml, 4)
         line["measured_peaks"] = peaks
     tr = measured_traffic(w.name, tau)
     if tr is not None:

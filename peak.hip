@@ -2,7 +2,9 @@
 // program beside bench.py (not part of the library):
 //   - bf16 MFMA rate of v_mfma_f32_32x32x16_bf16 with register operands (one
 //     and two waves per SIMD) and with one LDS-fed operand per MFMA (one
-//     ds_read_b128 per MFMA, two waves per SIMD: the attention's feed);
+//     ds_read_b128 per MFMA, two waves per SIMD: the attention's feed), with
+//     small-integer operands and with pseudo-random ones (the chip's clock
+//     under MFMA load depends on how many multiplier bits toggle);
 //   - fp32 MFMA rate of v_mfma_f32_32x32x2f32 with register operands;
 //   - HBM: a 1 GiB device copy (read + write) and a 1 GiB stream read;
 //   - the decode attention's read pattern over a K/V cache of [L][Hkv][128]
@@ -35,18 +37,32 @@ constexpr int kAcc = 8;          // independent accumulators per wave
 constexpr int kLdsSlots = 32;    // 1 KiB operand slots per wave, read round-robin
 constexpr int kLdsBytes = 96 * 1024;  // > 80 KiB: one workgroup per CU
 
+// A pseudo-random value in [-2, 2) from (seed, index), by a 32-bit integer
+// hash (xorshift-multiply); operands drawn from it toggle every multiplier
+// bit the way real activations do, where small-integer operands would not.
+__device__ __forceinline__ float hash_value(uint32_t seed, uint32_t i) {
+  uint32_t x = seed * 0x9E3779B9u ^ (i + 0x7F4A7C15u);
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return (float)(x >> 8) * (4.0f / 16777216.0f) - 2.0f;
+}
+
 // Register operands: NACC independent MFMA chains per wave. The operands come
-// from the thread index, and the accumulators are stored at the end, so
-// nothing can be folded away.
-template <int THREADS>
+// from the thread index (small integers, or pseudo-random values with RAND),
+// and the accumulators are stored at the end, so nothing can be folded away.
+template <int THREADS, bool RAND>
 __global__ void __launch_bounds__(THREADS) mfma_bf16_reg(int iters, float* out) {
   extern __shared__ uint8_t lds_pad[];  // sized by the launch to force one workgroup per CU
   (void)lds_pad;
   const int t = threadIdx.x;
+  const uint32_t gt = blockIdx.x * THREADS + t;
   bf16x8 a, b;
   for (int e = 0; e < 8; ++e) {
-    a[e] = (__bf16)(float)((t + e) & 7);
-    b[e] = (__bf16)(float)((t * 3 + e) & 7);
+    a[e] = (__bf16)(RAND ? hash_value(1, gt * 8 + e) : (float)((t + e) & 7));
+    b[e] = (__bf16)(RAND ? hash_value(2, gt * 8 + e) : (float)((t * 3 + e) & 7));
   }
   f32x16 acc[kAcc];
   for (int n = 0; n < kAcc; ++n) acc[n] = f32x16{};
@@ -63,19 +79,21 @@ __global__ void __launch_bounds__(THREADS) mfma_bf16_reg(int iters, float* out) 
 // One LDS-fed A operand per MFMA: each wave reads 16 bytes per lane from a
 // rotating 1 KiB slot (the address changes every MFMA, so no read can be
 // hoisted out of the loop), B stays in registers.
-template <int THREADS>
+template <int THREADS, bool RAND>
 __global__ void __launch_bounds__(THREADS) mfma_bf16_lds(int iters, float* out) {
   extern __shared__ uint8_t lds[];
   const int t = threadIdx.x, lane = t & 63;
+  const uint32_t gt = blockIdx.x * THREADS + t;
   // fill the kLdsSlots * 1 KiB operand area (every wave reads the same one)
   for (int i = t; i < kLdsSlots * 64; i += THREADS) {
     bf16x8 x;
-    for (int e = 0; e < 8; ++e) x[e] = (__bf16)(float)((i + e) & 7);
+    for (int e = 0; e < 8; ++e)
+      x[e] = (__bf16)(RAND ? hash_value(3, (blockIdx.x * kLdsSlots * 64 + i) * 8 + e) : (float)((i + e) & 7));
     *reinterpret_cast<bf16x8*>(lds + (size_t)i * 16) = x;
   }
   __syncthreads();
   bf16x8 b;
-  for (int e = 0; e < 8; ++e) b[e] = (__bf16)(float)((t * 3 + e) & 7);
+  for (int e = 0; e < 8; ++e) b[e] = (__bf16)(RAND ? hash_value(4, gt * 8 + e) : (float)((t * 3 + e) & 7));
   f32x16 acc[kAcc];
   for (int n = 0; n < kAcc; ++n) acc[n] = f32x16{};
   // operand reads run kRing MFMAs ahead through a register ring, the issue
@@ -163,6 +181,7 @@ static float best_ms(F launch, int reps) {
 
 struct Summary {
   double bf16_reg_1w = 0, bf16_reg_2w = 0, bf16_lds_2w = 0, f32_reg_2w = 0;
+  double bf16_reg_2w_rand = 0, bf16_lds_2w_rand = 0;
   double copy_GBps = 0, read_GBps = 0;
   double cache_stream_GBps = 0, cache_walk_GBps = 0;
   int ncu = 0, clock_khz = 0;
@@ -174,11 +193,15 @@ static void run_mfma(Summary& s) {
   const int iters = 4096;
   float* out = nullptr;
   CHECK(hipMalloc(&out, (size_t)grid * 512 * sizeof(float)));
-  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<256>),
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<256, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
-  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<512>),
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<512, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
-  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<512>),
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<512, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<512, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<512, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
   CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_f32_reg<512>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
@@ -186,19 +209,29 @@ static void run_mfma(Summary& s) {
   auto rate = [&](double flop_per_mfma, int threads, float ms) {
     return flop_per_mfma * kAcc * iters * (double)grid * (threads / 64) / (ms * 1e-3) / 1e12;
   };
-  float ms = best_ms([&] { mfma_bf16_reg<256><<<grid, 256, kLdsBytes>>>(iters, out); }, 5);
+  float ms = best_ms([&] { mfma_bf16_reg<256, false><<<grid, 256, kLdsBytes>>>(iters, out); }, 5);
   s.bf16_reg_1w = rate(f_bf16, 256, ms);
   printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"registers\", \"waves_per_simd\": 1, \"TFLOPs\": %.1f}\n",
          s.bf16_reg_1w);
-  ms = best_ms([&] { mfma_bf16_reg<512><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
+  ms = best_ms([&] { mfma_bf16_reg<512, false><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
   s.bf16_reg_2w = rate(f_bf16, 512, ms);
   printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"registers\", \"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
          s.bf16_reg_2w);
-  ms = best_ms([&] { mfma_bf16_lds<512><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
+  ms = best_ms([&] { mfma_bf16_reg<512, true><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
+  s.bf16_reg_2w_rand = rate(f_bf16, 512, ms);
+  printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"registers, pseudo-random operands\", "
+         "\"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
+         s.bf16_reg_2w_rand);
+  ms = best_ms([&] { mfma_bf16_lds<512, false><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
   s.bf16_lds_2w = rate(f_bf16, 512, ms);
   printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"one ds_read_b128 A operand per MFMA\", "
          "\"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
          s.bf16_lds_2w);
+  ms = best_ms([&] { mfma_bf16_lds<512, true><<<grid, 512, kLdsBytes>>>(iters, out); }, 5);
+  s.bf16_lds_2w_rand = rate(f_bf16, 512, ms);
+  printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"one ds_read_b128 A operand per MFMA, pseudo-random "
+         "operands\", \"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
+         s.bf16_lds_2w_rand);
   ms = best_ms([&] { mfma_f32_reg<512><<<grid, 512, kLdsBytes>>>(iters / 2, out); }, 5);
   s.f32_reg_2w = f_f32 * kAcc * (iters / 2) * (double)grid * 8 / (ms * 1e-3) / 1e12;
   printf("{\"probe\": \"mfma_f32_32x32x2\", \"feed\": \"registers\", \"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
@@ -323,10 +356,13 @@ int main(int argc, char** argv) {
   if (all || !strcmp(what, "hbm")) run_hbm(s);
   if (!strcmp(what, "cache")) run_cache(s, L, H);
   printf("{\"summary\": {\"cus\": %d, \"max_clock_mhz\": %d, \"mfma_bf16_reg_1w_TFLOPs\": %.1f, "
-         "\"mfma_bf16_reg_2w_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_TFLOPs\": %.1f, \"mfma_f32_reg_2w_TFLOPs\": %.2f, "
+         "\"mfma_bf16_reg_2w_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_TFLOPs\": %.1f, "
+         "\"mfma_bf16_reg_2w_random_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_random_TFLOPs\": %.1f, "
+         "\"mfma_f32_reg_2w_TFLOPs\": %.2f, "
          "\"hbm_copy_GBps\": %.1f, \"hbm_read_GBps\": %.1f, \"cache_stream_GBps\": %.1f, "
          "\"cache_walk_GBps\": %.1f}}\n",
-         s.ncu, s.clock_khz / 1000, s.bf16_reg_1w, s.bf16_reg_2w, s.bf16_lds_2w, s.f32_reg_2w, s.copy_GBps,
+         s.ncu, s.clock_khz / 1000, s.bf16_reg_1w, s.bf16_reg_2w, s.bf16_lds_2w, s.bf16_reg_2w_rand,
+         s.bf16_lds_2w_rand, s.f32_reg_2w, s.copy_GBps,
          s.read_GBps, s.cache_stream_GBps, s.cache_walk_GBps);
   return 0;
 }
