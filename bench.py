@@ -57,6 +57,76 @@ def measured_traffic(workload_name: str, tau: float, record: str = "attn_bf16", 
     return float(rec["traffic_bytes"]), float(rec["algorithmic_bytes"])
 
 
+def _pmc_rows(run_dir: str):
+    """Per-dispatch counter sums of a rocprofv3 --pmc run (its counter_collection.csv):
+    [(kernel name, duration ns, {counter: value})] in dispatch order."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    agg, meta = {}, {}
+    for r in csv.DictReader(open(files[0])):
+        k = int(r["Dispatch_Id"])
+        agg.setdefault(k, {})
+        agg[k][r["Counter_Name"]] = agg[k].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        meta[k] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return [(meta[k][0], meta[k][1], agg[k]) for k in sorted(agg)]
+
+
+def write_traffic_record(args):
+    """profiles/attn_bf16_<workload>_traffic.json from three rocprofv3 --pmc runs of
+    `bench.py --steps 1 --warmup 0 --calib-copy ...` (FETCH_SIZE, WRITE_SIZE, and the
+    SQ/GRBM counters): the attention kernel's counters scaled by what the same counters
+    read for the plain 1 GiB copy that runs first, plus its clock and MFMA busy."""
+    import hashlib
+
+    from synthetic.gen import workload
+
+    w = workload(args.workload)
+    tau = args.tau if args.tau is not None else w.taus[len(w.taus) // 2]
+    dirs = args.traffic_record
+    runs = [_pmc_rows(d) for d in dirs]
+
+    def pick(rows, key):
+        return [r for r in rows if key in r[0]]
+
+    copy_f = pick(runs[0], "copyBuffer")[0][2]["FETCH_SIZE"]
+    copy_w = pick(runs[1], "copyBuffer")[0][2]["WRITE_SIZE"]
+    att_f = [r[2]["FETCH_SIZE"] for r in pick(runs[0], "attn_bf16_pp_kernel")]
+    att_w = [r[2]["WRITE_SIZE"] for r in pick(runs[1], "attn_bf16_pp_kernel")]
+    gib_kib = float(1 << 20)
+    fs, ws_ = gib_kib / copy_f, gib_kib / copy_w
+    f = float(np.median(att_f)) * 1024 * fs
+    wr = float(np.median(att_w)) * 1024 * ws_
+    alg = 2 * (w.L * w.Hq * w.d * 2) + 2 * (w.L * w.Hkv * w.d * 2)  # Q, O and K, V once each
+    src = os.path.join(ROOT, "dynamic_block_sparse_rr_amd", "csrc", "attn.hip")
+    rec = {
+        "kernel": "attn_bf16_pp_kernel<%d,%d>" % (w.d, w.B), "workload": w.name, "tau": tau,
+        "kernel_source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+        "fetch_size_kib": float(np.median(att_f)), "write_size_kib": float(np.median(att_w)),
+        "copy_1GiB_fetch_size_kib": copy_f, "copy_1GiB_write_size_kib": copy_w,
+        "fetch_scale": fs, "write_scale": ws_, "hbm_fetch_bytes": f, "hbm_write_bytes": wr,
+        "traffic_bytes": f + wr, "algorithmic_bytes": alg,
+    }
+    if len(runs) > 2:
+        att = pick(runs[2], "attn_bf16_pp_kernel")[0]
+        cp = pick(runs[2], "copyBuffer")[0]
+        rec["sq"] = {k: att[2][k] for k in sorted(att[2])}
+        if "GRBM_GUI_ACTIVE" in att[2]:  # summed over the 8 XCDs
+            rec["core_clock_ghz_during_attention"] = att[2]["GRBM_GUI_ACTIVE"] / 8 / att[1]
+            rec["core_clock_ghz_during_copy"] = cp[2]["GRBM_GUI_ACTIVE"] / 8 / cp[1]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in att[2]:
+                ncu = 256
+                rec["mfma_busy"] = att[2]["SQ_VALU_MFMA_BUSY_CYCLES"] / (att[2]["GRBM_GUI_ACTIVE"] / 8 * ncu * 4)
+    path = os.path.join(ROOT, "profiles", "attn_bf16_%s_traffic.json" % w.name)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({k: rec[k] for k in ("workload", "traffic_bytes", "algorithmic_bytes")}), flush=True)
+
+
 def computed_flops(rc: np.ndarray, ci: np.ndarray, B: int, d: int, causal: bool):
     """(F_comp, blocks computed, diagonal blocks computed) from the block lists."""
     Hq, nb = rc.shape
@@ -208,7 +278,12 @@ def bench_varlen(args):
     from synthetic.gen import Workload, make_inputs
 
     lens = VARLEN_LENS
-    assert sum(lens) == 131072
+    if args.varlen_lens:  # "a,b,c" or "LxN" (N sequences of L tokens)
+        if "x" in args.varlen_lens:
+            L_, n_ = args.varlen_lens.split("x")
+            lens = [int(L_)] * int(n_)
+        else:
+            lens = [int(t) for t in args.varlen_lens.split(",")]
     tau = args.tau if args.tau is not None else 0.9
     parts = [make_inputs(Workload("llama8b_seq%d" % b, L, 32, 8, 128, "bf16", 128, 16, (tau,), 40 + b, "llm", 64))
              for b, L in enumerate(lens)]
@@ -253,15 +328,40 @@ def bench_varlen(args):
         roff += 32 * nb
         coff += 32 * nb * nb
     value = f_comp / (ms * 1e-3) / 1e12
+
+    # beside it, untimed in the line's value: the same sequences, one rr_prefill call each
+    offs = np.cumsum([0] + lens)
+    ps = [rr.problem(L, 32, 8, 128, 16, 128, tau, True, "bf16") for L in lens]
+    rcs = [torch.empty((32 * n,), dtype=torch.int32, device="cuda") for n in nbs]
+    cis = [torch.empty((32 * n * n,), dtype=torch.int32, device="cuda") for n in nbs]
+    ws1 = torch.empty(max(rr.rr_workspace_bytes(x) for x in ps), dtype=torch.uint8, device="cuda")
+
+    def step_each():
+        for b, L in enumerate(lens):
+            a, e = int(offs[b]), int(offs[b + 1])
+            rr.rr_prefill(ps[b], q[a:e], k[a:e], v[a:e], out[a:e], rcs[b], cis[b], ws1, stream=stream)
+
+    for _ in range(args.warmup):
+        step_each()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_each()
+    torch.cuda.synchronize()
+    ms_each = (time.perf_counter() - t0) * 1e3 / args.steps
+    del ws1
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama8b_varlen_batch_128k", "seq_lens": lens, "Hq": 32, "Hkv": 8, "d": 128,
+        "config": {"workload": "llama8b_varlen_batch_%dk" % (sum(lens) // 1024), "seq_lens": lens, "Hq": 32, "Hkv": 8, "d": 128,
                    "B": 128, "S": 16, "tau": tau, "causal": True},
         "step_ms_median_events": round(float(np.median(ev_ms)), 3),
         "blocks_computed_pct": round(100.0 * blocks / cand, 2),
-        "note": "rr_prefill_varlen: the searches one after the other, the attention of all sequences in one launch",
+        "note": ("rr_prefill_varlen: the searches one after the other; the attention of each sequence long enough to "
+                 "fill the GPU alone in a launch of its own, the others in one shared launch"),
+        "per_sequence_calls_ms": round(ms_each, 3),
+        "per_sequence_calls_tflops": round(f_comp / (ms_each * 1e-3) / 1e12, 2),
     }
     print(json.dumps(line), flush=True)
 
@@ -375,6 +475,8 @@ def main():
     ap.add_argument("--varlen", action="store_true",
                     help="a packed batch of LLaMA-8B-shaped sequences of ragged lengths (about 128K tokens in "
                          "all) through rr_prefill_varlen instead of one sequence")
+    ap.add_argument("--varlen-lens", default=None,
+                    help="with --varlen: the sequence lengths, as a,b,c or LxN (N sequences of L tokens)")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step against the 128K cache (rr_decode, pooled keys given) instead of prefill")
     ap.add_argument("--cold", action="store_true",
@@ -385,10 +487,16 @@ def main():
                          "shape, the practical read ceiling of the decode attention")
     ap.add_argument("--no-peak", action="store_true",
                     help="skip the measured MFMA/HBM peaks (peak.hip) that the roofline also divides by")
+    ap.add_argument("--traffic-record", nargs="+", default=None, metavar="PMC_DIR",
+                    help="write profiles/attn_bf16_<workload>_traffic.json from the output directories of "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, optionally the SQ/GRBM counters) of "
+                         "this script with --calib-copy; runs nothing on the GPU")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy, the reference kernel for "
                          "scaling HBM byte counters")
     args = ap.parse_args()
+    if args.traffic_record:
+        return write_traffic_record(args)
     if args.hbm_ceiling:  # a child process of its own, before this one touches the GPU
         import subprocess
 

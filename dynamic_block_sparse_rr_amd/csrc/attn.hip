@@ -1200,6 +1200,8 @@ hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_
   return hipGetLastError();
 }
 
+hipError_t attn_cu_count(hipStream_t st, int* ncu) { return stream_cu_count(st, ncu); }
+
 bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128 && g.Hq / g.Hkv >= 2; }
 
 int attn_items(const Geometry& g) {

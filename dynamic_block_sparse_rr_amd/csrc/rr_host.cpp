@@ -246,49 +246,6 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
       return RR_ERR_UNSUPPORTED;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // the search of each sequence, one after the other (they share the
-  // workspace's pooled-key and mass regions)
-  size_t tok = 0, rc_off = 0, ci_off = 0;
-  for (int32_t b = 0; b < n_seq; ++b) {
-    rr_problem pb = *p;
-    pb.L = seq_lens[b];
-    rr::Geometry g;
-    make_geometry(&pb, &g);
-    const uint8_t* qb = static_cast<const uint8_t*>(q) + tok * p->Hq * p->d * esz;
-    const uint8_t* kb = static_cast<const uint8_t*>(k) + tok * p->Hkv * p->d * esz;
-    s = run_search(g, qb, kb, row_count + rc_off, col_idx + ci_off, nullptr, nullptr, ws, st);
-    if (s != RR_OK) return s;
-    tok += seq_lens[b];
-    rc_off += (size_t)g.Hq * g.nb;
-    ci_off += (size_t)g.Hq * g.nb * g.nb;
-  }
-  rr_problem p0 = *p;
-  p0.L = seq_lens[0];
-  rr::Geometry g0;
-  make_geometry(&p0, &g0);
-  if (!vw.batched) {  // the other kernels: one attention launch per sequence
-    tok = rc_off = ci_off = 0;
-    for (int32_t b = 0; b < n_seq; ++b) {
-      rr_problem pb = *p;
-      pb.L = seq_lens[b];
-      rr::Geometry g;
-      make_geometry(&pb, &g);
-      const uint8_t* qb = static_cast<const uint8_t*>(q) + tok * p->Hq * p->d * esz;
-      const uint8_t* kb = static_cast<const uint8_t*>(k) + tok * p->Hkv * p->d * esz;
-      const uint8_t* vb = static_cast<const uint8_t*>(v) + tok * p->Hkv * p->d * esz;
-      uint8_t* ob = static_cast<uint8_t*>(out) + tok * p->Hq * p->d * esz;
-      s = run_attention(g, qb, kb, vb, row_count + rc_off, col_idx + ci_off, ob, ws, st);
-      if (s != RR_OK) return s;
-      tok += seq_lens[b];
-      rc_off += (size_t)g.Hq * g.nb;
-      ci_off += (size_t)g.Hq * g.nb * g.nb;
-    }
-    return RR_OK;
-  }
-  // The head-pair attention of every sequence in one launch (per group of
-  // kMaxSeqPerLaunch), after one V re-layout launch for the group: longest
-  // sequences first, so the launch starts with the longest rows, each
-  // sequence's work items on a range of their own.
   struct Seq {
     int32_t len;
     size_t tok, rc, ci, vt;
@@ -296,24 +253,76 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
   Seq seqs_small[64];
   Seq* seqs = n_seq <= 64 ? seqs_small : new (std::nothrow) Seq[n_seq];
   if (!seqs) return RR_ERR_INVALID_ARG;
-  tok = rc_off = ci_off = 0;
-  size_t vt_off = 0;
-  for (int32_t b = 0; b < n_seq; ++b) {
+  struct Free {
+    Seq *p, *keep;
+    ~Free() {
+      if (p != keep) delete[] p;
+    }
+  } free_seqs{seqs, seqs_small};
+  {
+    size_t tok = 0, rc_off = 0, ci_off = 0, vt_off = 0;
+    for (int32_t b = 0; b < n_seq; ++b) {
+      rr_problem pb = *p;
+      pb.L = seq_lens[b];
+      rr::Geometry g;
+      make_geometry(&pb, &g);
+      seqs[b] = Seq{seq_lens[b], tok, rc_off, ci_off, vt_off};
+      tok += seq_lens[b];
+      rc_off += (size_t)g.Hq * g.nb;
+      ci_off += (size_t)g.Hq * g.nb * g.nb;
+      vt_off += align_up(vt_bytes(g));
+    }
+  }
+  auto geometry = [&](const Seq& sq) {
     rr_problem pb = *p;
-    pb.L = seq_lens[b];
+    pb.L = sq.len;
     rr::Geometry g;
     make_geometry(&pb, &g);
-    seqs[b] = Seq{seq_lens[b], tok, rc_off, ci_off, vt_off};
-    tok += seq_lens[b];
-    rc_off += (size_t)g.Hq * g.nb;
-    ci_off += (size_t)g.Hq * g.nb * g.nb;
-    vt_off += align_up(vt_bytes(g));
+    return g;
+  };
+  // the sequences' searches share the workspace's pooled-key and mass regions,
+  // a single-sequence attention its V re-layout region: everything runs in
+  // stream order, so no two of them use one region at once
+  auto search = [&](const Seq& sq) {
+    return run_search(geometry(sq), static_cast<const uint8_t*>(q) + sq.tok * p->Hq * p->d * esz,
+                      static_cast<const uint8_t*>(k) + sq.tok * p->Hkv * p->d * esz, row_count + sq.rc,
+                      col_idx + sq.ci, nullptr, nullptr, ws, st);
+  };
+  auto attend = [&](const Seq& sq) {
+    return run_attention(geometry(sq), static_cast<const uint8_t*>(q) + sq.tok * p->Hq * p->d * esz,
+                         static_cast<const uint8_t*>(k) + sq.tok * p->Hkv * p->d * esz,
+                         static_cast<const uint8_t*>(v) + sq.tok * p->Hkv * p->d * esz, row_count + sq.rc,
+                         col_idx + sq.ci, static_cast<uint8_t*>(out) + sq.tok * p->Hq * p->d * esz, ws, st);
+  };
+  if (!vw.batched) {  // the other kernels: each sequence searched and attended in turn
+    for (int32_t b = 0; b < n_seq; ++b) {
+      if ((s = search(seqs[b])) != RR_OK || (s = attend(seqs[b])) != RR_OK) return s;
+    }
+    return RR_OK;
   }
+  // Head-pair attention, longest sequences first: a sequence with at least
+  // kVarlenSoloItemsPerCU work items per CU is searched and attended in
+  // launches of its own (a single-sequence launch fills the GPU and can
+  // balance its XCDs through the work queues); the others are searched one
+  // after the other and attended together in one launch per group of
+  // kMaxSeqPerLaunch, after one V re-layout launch for the group, each
+  // sequence's work items on a range of their own.
   std::stable_sort(seqs, seqs + n_seq, [](const Seq& a, const Seq& b) { return a.len > b.len; });
+  int ncu = 0;
+  hipError_t e = rr::attn_cu_count(st, &ncu);
+  if (e != hipSuccess) return hip_status(e);
+  int32_t nsolo = 0;
+  while (nsolo < n_seq &&
+         (long long)rr::attn_items(geometry(seqs[nsolo])) >= (long long)rr::kVarlenSoloItemsPerCU * ncu) {
+    if ((s = search(seqs[nsolo])) != RR_OK || (s = attend(seqs[nsolo])) != RR_OK) return s;
+    ++nsolo;
+  }
+  for (int32_t b = nsolo; b < n_seq; ++b)
+    if ((s = search(seqs[b])) != RR_OK) return s;
+  const rr::Geometry g0 = geometry(seqs[0]);
   uint8_t* vt = static_cast<uint8_t*>(ws) + vw.vt_base;
   int32_t* queues = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + vw.queues);
-  hipError_t e = hipSuccess;
-  for (int32_t b0 = 0; b0 < n_seq && e == hipSuccess; b0 += rr::kMaxSeqPerLaunch) {
+  for (int32_t b0 = nsolo; b0 < n_seq && e == hipSuccess; b0 += rr::kMaxSeqPerLaunch) {
     rr::SeqBatch sb;
     sb.n = std::min<int32_t>(rr::kMaxSeqPerLaunch, n_seq - b0);
     int items = 0, tiles = 0;
@@ -339,7 +348,6 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
     e = rr::launch_transpose_v_batched(g0, sb, v, vt, queues, st);
     if (e == hipSuccess) e = rr::launch_attention_batched(g0, sb, q, k, vt, queues, row_count, col_idx, out, st);
   }
-  if (seqs != seqs_small) delete[] seqs;
   return hip_status(e);
 }
 

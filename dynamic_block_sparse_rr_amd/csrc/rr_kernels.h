@@ -55,6 +55,12 @@ struct SeqBatch {
 constexpr int kAttnQueues = 8;
 bool attn_pair_shape(const Geometry& g);  // bf16, B = 128, two or more query heads per KV head
 int attn_items(const Geometry& g);        // work items of one sequence's head-pair launch
+hipError_t attn_cu_count(hipStream_t st, int* ncu);  // CUs of the stream's device (looked up once per device)
+// A sequence of a packed batch whose head-pair launch holds at least this
+// many work items per CU gets a launch of its own (it fills the GPU alone and
+// can balance its XCDs through the work queues); the shorter ones share
+// batched launches, where one launch fills the GPU for all of them.
+constexpr int kVarlenSoloItemsPerCU = 8;
 hipError_t launch_transpose_v(const Geometry& g, const void* v, void* vt, int32_t* queues, hipStream_t st);
 hipError_t launch_attention(const Geometry& g, const void* q, const void* k, const void* v,
                             const void* vt, int32_t* queues, const int32_t* row_count,

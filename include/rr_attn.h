@@ -185,10 +185,12 @@ rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, co
  * offset sum_{b'<b} Hq nb_b', col_idx at sum_{b'<b} Hq nb_b'^2, with
  * nb_b = ceil(L_b / B). Every sequence's slices must stay 16-byte aligned
  * (else RR_ERR_UNSUPPORTED). The searches run one after the other on the
- * stream; the attention of the whole batch is one launch (per 32 sequences)
- * where the problem has the head-pair kernel (bf16, B = 128, two or more
- * query heads per KV head), longest sequences first, else one launch per
- * sequence. One workspace of rr_workspace_bytes_varlen bytes serves them all
+ * stream. Where the problem has the head-pair kernel (bf16, B = 128, two or
+ * more query heads per KV head), the attention runs longest sequences first:
+ * a sequence with at least 8 work items per compute unit (about 16K tokens
+ * at the LLaMA-3.1-8B shape on 256 CUs) in a launch of its own, the others
+ * together in one launch per 32 sequences; else one launch per sequence.
+ * One workspace of rr_workspace_bytes_varlen bytes serves them all
  * (0 for an invalid batch). All lengths are checked before anything is
  * enqueued.
  */

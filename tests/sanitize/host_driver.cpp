@@ -129,6 +129,22 @@ int main() {
       bad = 1;
     }
     free(mws);
+    {  // one sequence long enough for a launch of its own (8 items per CU at 256 CUs), two batched
+      const int32_t mixed[3] = {70000, 1000, 333};
+      rr_problem px = {70000 + 1000 + 333, 8, 2, 128, 16, 128, 0.9f, 1, RR_BF16};
+      const size_t xneed = rr_workspace_bytes_varlen(&px, 3, mixed);
+      void* xws = workspace(xneed);
+      const long b0 = g_stub.batched_launches, s0 = g_stub.single_launches;
+      EXPECT(rr_prefill_varlen(&px, 3, mixed, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), xws, xneed,
+                               nullptr),
+             RR_OK);
+      if (g_stub.single_launches - s0 != 1 || g_stub.batched_launches - b0 != 1) {
+        fprintf(stderr, "mixed lengths: %ld solo and %ld batched launches\n", g_stub.single_launches - s0,
+                g_stub.batched_launches - b0);
+        bad = 1;
+      }
+      free(xws);
+    }
     rr_problem pf = {300 + 1000 + 128, 4, 4, 64, 8, 64, 0.9f, 1, RR_FP32};  // per-sequence attention
     const size_t fneed = rr_workspace_bytes_varlen(&pf, 3, lens);
     void* fws = workspace(fneed);

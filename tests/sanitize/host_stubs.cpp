@@ -56,6 +56,11 @@ hipError_t launch_union_lists(const Geometry&, const int32_t*, const int32_t*, i
 
 bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128 && g.Hq / g.Hkv >= 2; }
 
+hipError_t attn_cu_count(hipStream_t, int* ncu) {
+  *ncu = 256;
+  return hipSuccess;
+}
+
 int attn_items(const Geometry& g) {
   const int G = g.Hq / g.Hkv;
   return G % 2 ? g.Hkv * ((g.nb + 1) / 2) * G : g.Hkv * g.nb * (G / 2);
@@ -71,6 +76,7 @@ hipError_t launch_transpose_v(const Geometry& g, const void*, void* vt, int32_t*
 hipError_t launch_attention(const Geometry& g, const void*, const void*, const void*, const void* vt,
                             int32_t* queues, const int32_t*, const int32_t*, void*, hipStream_t) {
   ++g_stub.calls;
+  ++g_stub.single_launches;
   if (g.bf16) {
     in_ws(vt, (size_t)g.nb * g.B * g.Hkv * g.d * esz(g), "V re-layout (attention)");
     in_ws(queues, kAttnQueues * sizeof(int32_t), "work-queue counters (attention)");

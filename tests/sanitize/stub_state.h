@@ -11,5 +11,6 @@ struct StubState {
   long calls = 0;
   long batched_launches = 0;  // head-pair attention launches over several sequences
   long batched_items = 0;
+  long single_launches = 0;   // attention launches over one sequence
 };
 extern StubState g_stub;

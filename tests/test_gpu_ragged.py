@@ -118,19 +118,24 @@ def _head(res, h):
                                res.total[h:h + 1], res.kbar)
 
 
-def test_varlen_batch_matches_single_sequences():
-    lens = [1000, 2048, 300, 1537]
-    base = g("varlen", sum(lens), 8, 2, 128, 16, 128, "bf16", kind="llm", seed=300)
-    parts = [make_inputs(Workload(f"seq{b}", L, 8, 2, 128, "bf16", 128, 16, (0.9,), 300 + b, "llm", 8))
-             for b, L in enumerate(lens)]
+def _varlen_case(lens, Hq, Hkv, seed, max_full_rows=20000):
+    """A packed batch through rr_prefill_varlen against each sequence run alone
+    (same kernels: lists and outputs bitwise equal) and against the oracle
+    (every row where a sequence has at most max_full_rows (token, head) rows,
+    else one row per (head, query block) plus 64 sampled rows)."""
+    from synthetic.rows import sample_rows, work_item_rows
+
+    ws_ = [Workload(f"seq{b}", L, Hq, Hkv, 128, "bf16", 128, 16, (0.9,), seed + b, "llm", 8)
+           for b, L in enumerate(lens)]
+    parts = [make_inputs(w_) for w_ in ws_]
     q = torch.cat([p_[0] for p_ in parts]).cuda()
     k = torch.cat([p_[1] for p_ in parts]).cuda()
     v = torch.cat([p_[2] for p_ in parts]).cuda()
-    p = rr.problem(sum(lens), 8, 2, 128, 16, 128, 0.9, True, "bf16")
+    p = rr.problem(sum(lens), Hq, Hkv, 128, 16, 128, 0.9, True, "bf16")
     nbs = [-(-L // 128) for L in lens]
-    rc = torch.full((sum(8 * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
-    ci = torch.full((sum(8 * n * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
-    out = torch.empty_like(q)
+    rc = torch.full((sum(Hq * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
+    ci = torch.full((sum(Hq * n * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
     ws = torch.empty(rr.rr_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
     rr.rr_prefill_varlen(p, lens, q, k, v, out, rc, ci, ws)
     torch.cuda.synchronize()
@@ -138,23 +143,38 @@ def test_varlen_batch_matches_single_sequences():
     tok = roff = coff = 0
     for b, L in enumerate(lens):
         nb = nbs[b]
-        w = Workload(f"seq{b}", L, 8, 2, 128, "bf16", 128, 16, (0.9,), 300 + b, "llm", 8)
-        one = DeviceCase(w, 0.9, inputs=parts[b])
+        one = DeviceCase(ws_[b], 0.9, inputs=parts[b])
         o1, rc1, ci1 = one.prefill()
-        rcb = rc[roff:roff + 8 * nb].reshape(8, nb)
-        cib = ci[coff:coff + 8 * nb * nb].reshape(8, nb, nb)
+        rcb = rc[roff:roff + Hq * nb].reshape(Hq, nb)
+        cib = ci[coff:coff + Hq * nb * nb].reshape(Hq, nb, nb)
         np.testing.assert_array_equal(rcb, rc1)
-        for h in range(8):
+        for h in range(Hq):
             for i in range(nb):
                 np.testing.assert_array_equal(cib[h, i, :rcb[h, i]], ci1[h, i, :rc1[h, i]])
         np.testing.assert_array_equal(out[tok:tok + L], o1)  # same kernels, same inputs: bitwise
         # and against the oracle
         orc = oracle.search(parts[b][0], parts[b][1], S=16, B=128, tau=0.9, round_bf16=True)
         assert checker.classify(rcb, cib, orc, 0.9)["fail"] == 0
-        want = oracle.attention(parts[b][0], parts[b][1], parts[b][2], rcb, cib, B=128)
-        mx, mean = checker.output_errors(out[tok:tok + L], want)
+        if L * Hq <= max_full_rows:
+            want = oracle.attention(parts[b][0], parts[b][1], parts[b][2], rcb, cib, B=128)
+            mx, mean = checker.output_errors(out[tok:tok + L], want)
+        else:
+            rows = np.concatenate([work_item_rows(L, Hq, 128, seed=seed + b), sample_rows(L, Hq, 128, 64, seed=seed + b)])
+            want = oracle.attention(parts[b][0], parts[b][1], parts[b][2], rcb, cib, B=128, rows=rows)
+            mx, mean = checker.output_errors(out[tok:tok + L][rows[:, 0], rows[:, 1]], want)
         say(f"  varlen seq {b} L={L}: max-abs {mx:.3e} mean-abs {mean:.3e}")
         assert mx <= 2e-2 and mean <= 2e-3
         tok += L
-        roff += 8 * nb
-        coff += 8 * nb * nb
+        roff += Hq * nb
+        coff += Hq * nb * nb
+
+
+def test_varlen_batch_matches_single_sequences():
+    _varlen_case([1000, 2048, 300, 1537], 8, 2, 300)
+
+
+def test_varlen_long_sequence_in_its_own_launch():
+    """17,000 tokens at the 8B shape hold 16 * 133 = 2,128 work items, over 8
+    per CU on 256 CUs: that sequence gets a launch of its own, the two short
+    ones share one."""
+    _varlen_case([17000, 3000, 999], 32, 8, 310)
