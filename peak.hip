@@ -11,7 +11,9 @@
 //     bf16 (a grid-stride stream and the per-(KV head, run of blocks) walk).
 // Every rate is the best of several timed repetitions (HIP events). Prints
 // one JSON line per measurement and a last line {"summary": {...}}.
-// Usage: peak [all|mfma|hbm|cache] [L] [Hkv]
+//   - (chains) the rate of one wave per SIMD with 1, 2, 4 or 8 independent
+//     accumulator chains.
+// Usage: peak [all|mfma|hbm|cache|chains] [L] [Hkv]
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -128,6 +130,31 @@ __global__ void __launch_bounds__(THREADS) mfma_bf16_lds(int iters, float* out) 
   out[(size_t)blockIdx.x * THREADS + t] = s;
 }
 
+// One wave per SIMD, register operands, NACC independent accumulator chains
+// (8 MFMAs per loop trip): how many chains one wave needs to keep the matrix
+// unit busy.
+template <int NACC>
+__global__ void __launch_bounds__(256) mfma_bf16_chains(int iters, float* out) {
+  extern __shared__ uint8_t lds_pad[];
+  (void)lds_pad;
+  const int t = threadIdx.x;
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(float)((t + e) & 7);
+    b[e] = (__bf16)(float)((t * 3 + e) & 7);
+  }
+  f32x16 acc[NACC];
+  for (int n = 0; n < NACC; ++n) acc[n] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j % NACC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j % NACC], 0, 0, 0);
+  }
+  float s = 0.0f;
+  for (int n = 0; n < NACC; ++n)
+    for (int v = 0; v < 16; ++v) s += acc[n][v];
+  out[(size_t)blockIdx.x * 256 + t] = s;
+}
+
 template <int THREADS>
 __global__ void __launch_bounds__(THREADS) mfma_f32_reg(int iters, float* out) {
   extern __shared__ uint8_t lds_pad[];
@@ -209,6 +236,8 @@ static void run_mfma(Summary& s) {
   auto rate = [&](double flop_per_mfma, int threads, float ms) {
     return flop_per_mfma * kAcc * iters * (double)grid * (threads / 64) / (ms * 1e-3) / 1e12;
   };
+  // about 70 ms of MFMA work first, so that the first timed probe does not see the clock still rising
+  (void)best_ms([&] { mfma_bf16_reg<512, false><<<grid, 512, kLdsBytes>>>(iters, out); }, 20);
   float ms = best_ms([&] { mfma_bf16_reg<256, false><<<grid, 256, kLdsBytes>>>(iters, out); }, 5);
   s.bf16_reg_1w = rate(f_bf16, 256, ms);
   printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"registers\", \"waves_per_simd\": 1, \"TFLOPs\": %.1f}\n",
@@ -335,12 +364,34 @@ static void run_cache(Summary& s, int L, int H) {
   CHECK(hipFree(out));
 }
 
+template <int NACC>
+static void run_chains_one(int ncu, float* out) {
+  const int grid = ncu * 4, iters = 4096;
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_chains<NACC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+  const float ms = best_ms([&] { mfma_bf16_chains<NACC><<<grid, 256, kLdsBytes>>>(iters, out); }, 5);
+  const double tf = 32.0 * 32 * 16 * 2 * 8 * iters * (double)grid * 4 / (ms * 1e-3) / 1e12;
+  printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"registers\", \"waves_per_simd\": 1, \"chains\": %d, "
+         "\"TFLOPs\": %.1f}\n", NACC, tf);
+}
+
+static void run_chains(int ncu) {
+  float* out = nullptr;
+  CHECK(hipMalloc(&out, (size_t)ncu * 4 * 256 * sizeof(float)));
+  run_chains_one<8>(ncu, out);  // also brings the clock up before the others
+  run_chains_one<1>(ncu, out);
+  run_chains_one<2>(ncu, out);
+  run_chains_one<4>(ncu, out);
+  run_chains_one<8>(ncu, out);
+  CHECK(hipFree(out));
+}
+
 int main(int argc, char** argv) {
   const char* what = argc > 1 ? argv[1] : "all";
   const int L = argc > 2 ? atoi(argv[2]) : 131072, H = argc > 3 ? atoi(argv[3]) : 8;
   const bool all = !strcmp(what, "all");
-  if (!all && strcmp(what, "mfma") && strcmp(what, "hbm") && strcmp(what, "cache")) {
-    fprintf(stderr, "usage: peak [all|mfma|hbm|cache] [L] [Hkv]\n");
+  if (!all && strcmp(what, "mfma") && strcmp(what, "hbm") && strcmp(what, "cache") && strcmp(what, "chains")) {
+    fprintf(stderr, "usage: peak [all|mfma|hbm|cache|chains] [L] [Hkv]\n");
     return 2;
   }
   if (L < 128 || L % 128 != 0 || H < 1 || (long long)L * H > (1ll << 26)) {
@@ -355,6 +406,7 @@ int main(int argc, char** argv) {
   if (all || !strcmp(what, "mfma")) run_mfma(s);
   if (all || !strcmp(what, "hbm")) run_hbm(s);
   if (!strcmp(what, "cache")) run_cache(s, L, H);
+  if (!strcmp(what, "chains")) run_chains(s.ncu);
   printf("{\"summary\": {\"cus\": %d, \"max_clock_mhz\": %d, \"mfma_bf16_reg_1w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_random_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_random_TFLOPs\": %.1f, "
