@@ -197,7 +197,7 @@ static rr_status varlen_geometries(const rr_problem* p, int32_t n_seq, const int
                                    VarlenWorkspace* vw) {
   if (!p || n_seq <= 0 || !seq_lens) return RR_ERR_INVALID_ARG;
   long long total = 0;
-  size_t single = 0, search = 0, vts = 0;
+  size_t single = 0, search = 0, searches = 0, vts = 0;
   bool pair = false;
   for (int32_t b = 0; b < n_seq; ++b) {
     if (seq_lens[b] <= 0) return RR_ERR_INVALID_ARG;
@@ -208,13 +208,15 @@ static rr_status varlen_geometries(const rr_problem* p, int32_t n_seq, const int
     if (s != RR_OK) return s;
     const Workspace w = layout(g);
     single = std::max(single, w.total);
-    search = std::max(search, w.vt);  // pooled keys and masses
+    search = std::max(search, w.vt);  // pooled keys and masses of one sequence
+    searches += w.vt;                 // ... of every sequence at once (batched search)
     vts += align_up(vt_bytes(g));
     pair = rr::attn_pair_shape(g);
     total += seq_lens[b];
   }
   if (total != p->L) return RR_ERR_INVALID_ARG;
   vw->batched = pair;
+  if (pair) search = std::max(search, searches);
   vw->vt_base = search;
   vw->queues = search + vts;
   vw->total = pair ? vw->queues + align_up(rr::kAttnQueues * sizeof(int32_t)) : single;
@@ -317,11 +319,47 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
     if ((s = search(seqs[nsolo])) != RR_OK || (s = attend(seqs[nsolo])) != RR_OK) return s;
     ++nsolo;
   }
-  for (int32_t b = nsolo; b < n_seq; ++b)
-    if ((s = search(seqs[b])) != RR_OK) return s;
   const rr::Geometry g0 = geometry(seqs[0]);
   uint8_t* vt = static_cast<uint8_t*>(ws) + vw.vt_base;
   int32_t* queues = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + vw.queues);
+  // the other sequences' searches: pooled keys, scores and selection of up to
+  // kMaxSeqPerLaunch sequences per launch, each sequence's pooled keys and
+  // masses in a region of their own at the start of the workspace
+  for (int32_t b0 = nsolo; b0 < n_seq && e == hipSuccess; b0 += rr::kMaxSeqPerLaunch) {
+    rr::SearchBatch sbt;
+    sbt.n = std::min<int32_t>(rr::kMaxSeqPerLaunch, n_seq - b0);
+    int pool = 0, blk = 0, rows = 0;
+    size_t off = 0;
+    for (int m = 0; m < sbt.n; ++m) {
+      const Seq& sq = seqs[b0 + m];
+      const rr::Geometry g = geometry(sq);
+      const Workspace w = layout(g);
+      int np, nbk, nr;
+      rr::search_batch_counts(g, g.nb, g.ns, &np, &nbk, &nr);
+      sbt.pool_off[m] = pool;
+      sbt.blk_off[m] = blk;
+      sbt.row_off[m] = rows;
+      sbt.tok_off[m] = (int)sq.tok;
+      sbt.L[m] = sq.len;
+      sbt.nb[m] = g.nb;
+      sbt.ns[m] = g.ns;
+      sbt.kbar_off[m] = (long long)(off / esz);
+      sbt.mass_off[m] = (long long)((off + w.mass) / sizeof(float));
+      sbt.rc_off[m] = (long long)sq.rc;
+      sbt.ci_off[m] = (long long)sq.ci;
+      pool += np;
+      blk += nbk;
+      rows += nr;
+      off += w.vt;  // this sequence's pooled keys and masses
+    }
+    sbt.pool_off[sbt.n] = pool;
+    sbt.blk_off[sbt.n] = blk;
+    sbt.row_off[sbt.n] = rows;
+    float* mass = reinterpret_cast<float*>(ws);
+    e = rr::launch_pool_keys_batched(g0, sbt, k, ws, st);
+    if (e == hipSuccess) e = rr::launch_search_batched(g0, sbt, q, ws, mass, st);
+    if (e == hipSuccess) e = rr::launch_select_batched(g0, sbt, mass, row_count, col_idx, st);
+  }
   for (int32_t b0 = nsolo; b0 < n_seq && e == hipSuccess; b0 += rr::kMaxSeqPerLaunch) {
     rr::SeqBatch sb;
     sb.n = std::min<int32_t>(rr::kMaxSeqPerLaunch, n_seq - b0);

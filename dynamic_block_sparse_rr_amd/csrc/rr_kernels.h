@@ -27,6 +27,36 @@ hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, flo
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
                          int32_t* col_idx, const float* tau_heads, hipStream_t st);
 
+constexpr int kMaxSeqPerLaunch = 32;
+
+// The search of a packed batch of sequences (up to kMaxSeqPerLaunch) in one
+// launch per kernel: per sequence its first token, length, block and stride
+// counts, the offsets of its pooled keys (elements, chunk-major layout), its
+// block masses (floats) and its block lists (entries), and prefix counts of
+// the work of each launch (pool: threads, search: workgroups, select: rows;
+// entry n is the total). g describes the sequences but for L, nb and ns.
+struct SearchBatch {
+  int n;
+  int pool_off[kMaxSeqPerLaunch + 1];
+  int blk_off[kMaxSeqPerLaunch + 1];
+  int row_off[kMaxSeqPerLaunch + 1];
+  int tok_off[kMaxSeqPerLaunch];
+  int L[kMaxSeqPerLaunch];
+  int nb[kMaxSeqPerLaunch];
+  int ns[kMaxSeqPerLaunch];
+  long long kbar_off[kMaxSeqPerLaunch];
+  long long mass_off[kMaxSeqPerLaunch];
+  long long rc_off[kMaxSeqPerLaunch];
+  long long ci_off[kMaxSeqPerLaunch];
+};
+void search_batch_counts(const Geometry& g, int nb, int ns, int* pool_threads, int* search_blocks, int* rows);
+hipError_t launch_pool_keys_batched(const Geometry& g, const SearchBatch& sb, const void* k, void* kbar,
+                                    hipStream_t st);
+hipError_t launch_search_batched(const Geometry& g, const SearchBatch& sb, const void* q, const void* kbar,
+                                 float* mass, hipStream_t st);
+hipError_t launch_select_batched(const Geometry& g, const SearchBatch& sb, const float* mass, int32_t* row_count,
+                                 int32_t* col_idx, hipStream_t st);
+
 // Variant: every head of a KV head gets the union of the group's selections.
 hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const int32_t* col_idx,
                               int32_t* out_count, int32_t* out_idx, hipStream_t st);
@@ -36,7 +66,6 @@ hipError_t launch_union_lists(const Geometry& g, const int32_t* row_count, const
 // block count, the entry offsets of its block lists, the byte offset of its V
 // re-layout, the first of its work items (multiples of 16; item_off[n] is the
 // total) and the first of its V tiles (tile_off[n] is the total).
-constexpr int kMaxSeqPerLaunch = 32;
 struct SeqBatch {
   int n;
   int item_off[kMaxSeqPerLaunch + 1];

@@ -30,12 +30,25 @@
 //               the cut mass (see the kernel), then the kept blocks compacted
 //               into an ascending list.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "rr_kernels.h"
 
 namespace rr {
 namespace {
+
+struct NoSearchBatch {};
+template <bool VARLEN>
+using SearchBatchArg = typename std::conditional<VARLEN, SearchBatch, NoSearchBatch>::type;
+
+// Sequence of a packed batch whose range [off[b], off[b + 1]) holds x.
+__device__ __forceinline__ int batch_seq(const int* off, int n, long long x) {
+  int b = 0;
+  while (b + 1 < n && x >= off[b + 1]) ++b;
+  return b;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -59,10 +72,25 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float x) {
 // chunk-major [Hkv][d*sizeof(T)/16][ns] of 16-byte chunks (CM true: the
 // search's own copy, in which the 32 strides of one MFMA operand load are
 // contiguous).
-template <typename T, bool CM>
-__global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k, T* __restrict__ kbar,
-                                                        int ns, int row_chunks, int S, int L) {
-  const long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+// VARLEN: the threads of a packed batch of sequences (SearchBatch), each
+// sequence's pooled keys in a region of their own.
+template <typename T, bool CM, bool VARLEN>
+__global__ void __launch_bounds__(256) pool_keys_kernel(const T* __restrict__ k_all, T* __restrict__ kbar_all,
+                                                        int ns_all, int row_chunks, int S, int L_all,
+                                                        const SearchBatchArg<VARLEN> sb) {
+  long long n = (long long)blockIdx.x * 256 + threadIdx.x;
+  const T* k = k_all;
+  T* kbar = kbar_all;
+  int ns = ns_all, L = L_all;
+  if constexpr (VARLEN) {
+    if (n >= sb.pool_off[sb.n]) return;
+    const int b = batch_seq(sb.pool_off, sb.n, n);
+    n -= sb.pool_off[b];
+    k = k_all + (size_t)sb.tok_off[b] * row_chunks * (16 / sizeof(T));
+    kbar = kbar_all + sb.kbar_off[b];
+    ns = sb.ns[b];
+    L = sb.L[b];
+  }
   if (n >= (long long)ns * row_chunks) return;
   const int t = (int)(n / row_chunks);
   const int c = (int)(n % row_chunks);
@@ -162,11 +190,27 @@ __device__ __forceinline__ int out_row(int v, int half) { return 8 * (v >> 2) + 
 // CT: column tiles of sampled queries the kernel can hold (1 when a
 // workgroup's heads times R fit in 32 columns, which keeps the registers of
 // the second tile free).
-template <typename T, int D, int R, int CT>
-__global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, const T* __restrict__ kbar,
-                                                     float* __restrict__ mass, int Hq, int Hkv, int S,
-                                                     int nb, int ns, int causal, int hpc, int nchunk,
-                                                     float cscale) {
+// VARLEN: the workgroups of a packed batch of sequences (SearchBatch); each
+// workgroup decodes its sequence and continues as that sequence's own.
+template <typename T, int D, int R, int CT, bool VARLEN>
+__global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q_all, const T* __restrict__ kbar_all,
+                                                     float* __restrict__ mass_all, int Hq, int Hkv, int S,
+                                                     int nb_all, int ns_all, int causal, int hpc, int nchunk,
+                                                     float cscale, const SearchBatchArg<VARLEN> sb) {
+  int bid = blockIdx.x;
+  const T* q = q_all;
+  const T* kbar = kbar_all;
+  float* mass = mass_all;
+  int nb = nb_all, ns = ns_all;
+  if constexpr (VARLEN) {  // uniform per workgroup
+    const int b = batch_seq(sb.blk_off, sb.n, bid);
+    bid -= sb.blk_off[b];
+    q = q_all + (size_t)sb.tok_off[b] * Hq * D;
+    kbar = kbar_all + sb.kbar_off[b];
+    mass = mass_all + sb.mass_off[b];
+    nb = sb.nb[b];
+    ns = sb.ns[b];
+  }
   typedef typename Mfma<T>::chunk chunk_t;
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int NCH = D / (2 * E);   // chunks per lane per row (two lane halves split d)
@@ -176,8 +220,8 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q, co
   const int n32 = lane & 31, half = lane >> 5;
 
   // work item: long rows first
-  const int chunk = blockIdx.x % nchunk;
-  const int rest = blockIdx.x / nchunk;
+  const int chunk = bid % nchunk;
+  const int rest = bid / nchunk;
   const int g = rest % Hkv;
   const int i = (nb - 2) - rest / Hkv;
   const int G = Hq / Hkv;
@@ -401,15 +445,34 @@ __device__ __forceinline__ uint32_t mass_bits(float m) { return m > 0.0f ? __flo
 // rounding of the threshold. At least one block is kept (the first of the
 // order: the heaviest, lowest index) even when every mass is zero. The kept
 // blocks are written in ascending order (ballot and prefix count per 64).
-__global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass, int zero_fill,
-                                                     int32_t* __restrict__ row_count,
-                                                     int32_t* __restrict__ col_idx, int nrows, int nb, int causal,
-                                                     float tau_all, const float* __restrict__ tau_heads) {
-  extern __shared__ float srow_all[];  // one row of nb masses per wave
+// VARLEN: the rows of a packed batch of sequences (SearchBatch; no exported
+// masses, one threshold); each wave decodes its row's sequence. pitch: the
+// LDS floats per wave (the largest nb of the launch).
+template <bool VARLEN>
+__global__ void __launch_bounds__(256) select_kernel(float* __restrict__ mass_all, int zero_fill,
+                                                     int32_t* __restrict__ rc_all,
+                                                     int32_t* __restrict__ ci_all, int nrows, int nb_all,
+                                                     int causal, float tau_all, const float* __restrict__ tau_heads,
+                                                     int pitch, const SearchBatchArg<VARLEN> sb) {
+  extern __shared__ float srow_all[];  // one row of up to pitch masses per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= nrows) return;  // the whole wave; nothing below waits for the other waves
-  float* srow = srow_all + wave * nb;
+  int row = blockIdx.x * 4 + wave;
+  float* mass = mass_all;
+  int32_t* row_count = rc_all;
+  int32_t* col_idx = ci_all;
+  int nb = nb_all;
+  if constexpr (VARLEN) {  // uniform per wave
+    if (row >= sb.row_off[sb.n]) return;
+    const int b = batch_seq(sb.row_off, sb.n, row);
+    row -= sb.row_off[b];
+    mass = mass_all + sb.mass_off[b];
+    row_count = rc_all + sb.rc_off[b];
+    col_idx = ci_all + sb.ci_off[b];
+    nb = sb.nb[b];
+  } else {
+    if (row >= nrows) return;  // the whole wave; nothing below waits for the other waves
+  }
+  float* srow = srow_all + wave * pitch;
   const int i = row % nb;
   const int ncand = causal ? i + 1 : nb;
   float* mrow = mass + (size_t)row * nb;
@@ -770,11 +833,17 @@ __global__ void __launch_bounds__(256) decode_select_kernel(const float* __restr
   if (tid == 0) row_count[h] = (int32_t)(wt32[0] + wt32[1] + wt32[2] + wt32[3]);
 }
 
+// Query heads per search workgroup and workgroups per (query block, KV head).
+inline void search_split(const Geometry& g, int* hpc, int* nchunk) {
+  *hpc = min(g.G, 64 / g.r);
+  *nchunk = (g.G + *hpc - 1) / *hpc;
+}
+
 template <typename T, int D>
 hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, float* mass,
                            hipStream_t st) {
-  const int hpc = min(g.G, 64 / g.r);
-  const int nchunk = (g.G + hpc - 1) / hpc;
+  int hpc, nchunk;
+  search_split(g, &hpc, &nchunk);
   const int nrows = g.nb - 1;
   if (nrows <= 0) return hipSuccess;
   const dim3 grid((unsigned)(nrows * g.Hkv * nchunk));
@@ -782,14 +851,47 @@ hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, f
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(kbar);
   const bool one_tile = hpc * g.r <= 32;
-#define RR_SEARCH_CASE(RV)                                                                        \
-  case RV:                                                                                        \
-    if (one_tile)                                                                                 \
-      search_kernel<T, D, RV, 1><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
-                                                       g.causal, hpc, nchunk, cscale);           \
-    else                                                                                          \
-      search_kernel<T, D, RV, 2><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
-                                                       g.causal, hpc, nchunk, cscale);           \
+#define RR_SEARCH_CASE(RV)                                                                               \
+  case RV:                                                                                               \
+    if (one_tile)                                                                                        \
+      search_kernel<T, D, RV, 1, false><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
+                                                              g.causal, hpc, nchunk, cscale, {});        \
+    else                                                                                                 \
+      search_kernel<T, D, RV, 2, false><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, g.nb, g.ns, \
+                                                              g.causal, hpc, nchunk, cscale, {});        \
+    break;
+  switch (g.r) {
+    RR_SEARCH_CASE(2)
+    RR_SEARCH_CASE(4)
+    RR_SEARCH_CASE(8)
+    RR_SEARCH_CASE(16)
+    RR_SEARCH_CASE(32)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef RR_SEARCH_CASE
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_search_batched_r(const Geometry& g, const SearchBatch& sb, const void* q, const void* kbar,
+                                   float* mass, hipStream_t st) {
+  int hpc, nchunk;
+  search_split(g, &hpc, &nchunk);
+  if (sb.blk_off[sb.n] <= 0) return hipSuccess;
+  const dim3 grid((unsigned)sb.blk_off[sb.n]);
+  const float cscale = (1.0f / sqrtf((float)g.d)) * 1.4426950408889634f;
+  const T* qq = static_cast<const T*>(q);
+  const T* kk = static_cast<const T*>(kbar);
+  const bool one_tile = hpc * g.r <= 32;
+#define RR_SEARCH_CASE(RV)                                                                            \
+  case RV:                                                                                            \
+    if (one_tile)                                                                                     \
+      search_kernel<T, D, RV, 1, true><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, 0, 0,     \
+                                                             g.causal, hpc, nchunk, cscale, sb);      \
+    else                                                                                              \
+      search_kernel<T, D, RV, 2, true><<<grid, 256, 0, st>>>(qq, kk, mass, g.Hq, g.Hkv, g.S, 0, 0,     \
+                                                             g.causal, hpc, nchunk, cscale, sb);      \
     break;
   switch (g.r) {
     RR_SEARCH_CASE(2)
@@ -806,14 +908,57 @@ hipError_t launch_search_r(const Geometry& g, const void* q, const void* kbar, f
 
 }  // namespace
 
+void search_batch_counts(const Geometry& g, int nb, int ns, int* pool_threads, int* search_blocks, int* rows) {
+  int hpc, nchunk;
+  search_split(g, &hpc, &nchunk);
+  *pool_threads = ns * (g.Hkv * g.d * (g.bf16 ? 2 : 4) / 16);
+  *search_blocks = (nb - 1) * g.Hkv * nchunk;
+  *rows = g.Hq * nb;
+}
+
+hipError_t launch_pool_keys_batched(const Geometry& g, const SearchBatch& sb, const void* k, void* kbar,
+                                    hipStream_t st) {
+  const int row_chunks = g.Hkv * g.d * (g.bf16 ? 2 : 4) / 16;
+  const dim3 grid((unsigned)((sb.pool_off[sb.n] + 255) / 256));
+  if (g.bf16)
+    pool_keys_kernel<__bf16, true, true><<<grid, 256, 0, st>>>(static_cast<const __bf16*>(k), static_cast<__bf16*>(kbar),
+                                                               0, row_chunks, g.S, 0, sb);
+  else
+    pool_keys_kernel<float, true, true><<<grid, 256, 0, st>>>(static_cast<const float*>(k), static_cast<float*>(kbar),
+                                                              0, row_chunks, g.S, 0, sb);
+  return hipGetLastError();
+}
+
+hipError_t launch_search_batched(const Geometry& g, const SearchBatch& sb, const void* q, const void* kbar,
+                                 float* mass, hipStream_t st) {
+  if (g.bf16) return g.d == 128 ? launch_search_batched_r<__bf16, 128>(g, sb, q, kbar, mass, st)
+                                : launch_search_batched_r<__bf16, 64>(g, sb, q, kbar, mass, st);
+  return g.d == 128 ? launch_search_batched_r<float, 128>(g, sb, q, kbar, mass, st)
+                    : launch_search_batched_r<float, 64>(g, sb, q, kbar, mass, st);
+}
+
+hipError_t launch_select_batched(const Geometry& g, const SearchBatch& sb, const float* mass, int32_t* row_count,
+                                 int32_t* col_idx, hipStream_t st) {
+  int pitch = 1;
+  for (int b = 0; b < sb.n; ++b) pitch = max(pitch, sb.nb[b]);
+  const size_t lds = 4 * (size_t)pitch * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  if (sb.row_off[sb.n] <= 0) return hipSuccess;
+  select_kernel<true><<<dim3((unsigned)((sb.row_off[sb.n] + 3) / 4)), 256, lds, st>>>(
+      const_cast<float*>(mass), 0, row_count, col_idx, 0, 0, g.causal, g.tau, nullptr, pitch, sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_pool_keys(const Geometry& g, const void* k, void* kbar, bool chunk_major, hipStream_t st) {
   const int esz = g.bf16 ? 2 : 4;
   const int row_chunks = g.Hkv * g.d * esz / 16;
   const long long n = (long long)g.ns * row_chunks;
   const dim3 grid((unsigned)((n + 255) / 256));
-#define RR_POOL(TY, CMV)                                                                                   \
-  pool_keys_kernel<TY, CMV><<<grid, 256, 0, st>>>(static_cast<const TY*>(k), static_cast<TY*>(kbar), g.ns, \
-                                                  row_chunks, g.S, g.L)
+#define RR_POOL(TY, CMV)                                                                           \
+  pool_keys_kernel<TY, CMV, false><<<grid, 256, 0, st>>>(static_cast<const TY*>(k), static_cast<TY*>(kbar), \
+                                                         g.ns, row_chunks, g.S, g.L, {})
   if (g.bf16) {
     if (chunk_major) RR_POOL(__bf16, true);
     else RR_POOL(__bf16, false);
@@ -836,13 +981,12 @@ hipError_t launch_search(const Geometry& g, const void* q, const void* kbar, flo
 hipError_t launch_select(const Geometry& g, const float* mass, int zero_fill, int32_t* row_count,
                          int32_t* col_idx, const float* tau_heads, hipStream_t st) {
   const size_t lds = 4 * (size_t)g.nb * sizeof(float);  // one row per wave
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nrows = g.Hq * g.nb;
-  select_kernel<<<dim3((unsigned)((nrows + 3) / 4)), 256, lds, st>>>(const_cast<float*>(mass), zero_fill, row_count,
-                                                                      col_idx, nrows, g.nb, g.causal, g.tau,
-                                                                      tau_heads);
+  select_kernel<false><<<dim3((unsigned)((nrows + 3) / 4)), 256, lds, st>>>(
+      const_cast<float*>(mass), zero_fill, row_count, col_idx, nrows, g.nb, g.causal, g.tau, tau_heads, g.nb, {});
   return hipGetLastError();
 }
 

@@ -184,12 +184,13 @@ rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, co
  * of sequence b follow those of the sequences before it: row_count at entry
  * offset sum_{b'<b} Hq nb_b', col_idx at sum_{b'<b} Hq nb_b'^2, with
  * nb_b = ceil(L_b / B). Every sequence's slices must stay 16-byte aligned
- * (else RR_ERR_UNSUPPORTED). The searches run one after the other on the
- * stream. Where the problem has the head-pair kernel (bf16, B = 128, two or
- * more query heads per KV head), the attention runs longest sequences first:
- * a sequence with at least 8 work items per compute unit (about 16K tokens
- * at the LLaMA-3.1-8B shape on 256 CUs) in a launch of its own, the others
- * together in one launch per 32 sequences; else one launch per sequence.
+ * (else RR_ERR_UNSUPPORTED). Where the problem has the head-pair kernel
+ * (bf16, B = 128, two or more query heads per KV head), the sequences run
+ * longest first: one with at least 8 attention work items per compute unit
+ * (about 16K tokens at the LLaMA-3.1-8B shape on 256 CUs) is searched and
+ * attended in launches of its own, as rr_prefill would; the others are
+ * searched and attended together, one launch per kernel per 32 sequences.
+ * Otherwise each sequence is searched and attended in turn.
  * One workspace of rr_workspace_bytes_varlen bytes serves them all
  * (0 for an invalid batch). All lengths are checked before anything is
  * enqueued.

@@ -108,8 +108,9 @@ int main() {
   void* vws = workspace(vneed);
   EXPECT(rr_prefill_varlen(&pv, 3, lens, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), vws, vneed, nullptr),
          RR_OK);
-  if (g_stub.batched_launches != 1) {  // three sequences: one head-pair launch
-    fprintf(stderr, "varlen attention: %ld batched launches\n", g_stub.batched_launches);
+  if (g_stub.batched_launches != 1 || g_stub.batched_searches != 3) {  // three sequences: one launch per kernel
+    fprintf(stderr, "varlen: %ld batched attention launches, %ld batched search launches\n", g_stub.batched_launches,
+            g_stub.batched_searches);
     bad = 1;
   }
   free(vws);

@@ -49,6 +49,50 @@ hipError_t launch_select(const Geometry& g, const float* mass, int, int32_t*, in
   return hipSuccess;
 }
 
+void search_batch_counts(const Geometry& g, int nb, int ns, int* pool_threads, int* search_blocks, int* rows) {
+  const int hpc = g.G < 64 / g.r ? g.G : 64 / g.r;
+  *pool_threads = ns * (g.Hkv * g.d * (int)esz(g) / 16);
+  *search_blocks = (nb - 1) * g.Hkv * ((g.G + hpc - 1) / hpc);
+  *rows = g.Hq * nb;
+}
+
+// The batched search launches: every sequence's pooled keys and masses must lie
+// inside the workspace, the prefix counts must match the per-sequence counts.
+static void check_search_batch(const Geometry& g, const SearchBatch& sb, const void* kbar, const float* mass) {
+  if (sb.n < 1 || sb.n > kMaxSeqPerLaunch) abort();
+  for (int m = 0; m < sb.n; ++m) {
+    int np, nbk, nr;
+    search_batch_counts(g, sb.nb[m], sb.ns[m], &np, &nbk, &nr);
+    if (sb.pool_off[m + 1] - sb.pool_off[m] != np || sb.blk_off[m + 1] - sb.blk_off[m] != nbk ||
+        sb.row_off[m + 1] - sb.row_off[m] != nr)
+      abort();
+    in_ws(static_cast<const char*>(kbar) + sb.kbar_off[m] * esz(g), (size_t)sb.ns[m] * g.Hkv * g.d * esz(g),
+          "pooled keys (batched)");
+    in_ws(mass + sb.mass_off[m], (size_t)g.Hq * sb.nb[m] * sb.nb[m] * sizeof(float), "block masses (batched)");
+  }
+  ++g_stub.batched_searches;
+}
+
+hipError_t launch_pool_keys_batched(const Geometry& g, const SearchBatch& sb, const void*, void* kbar, hipStream_t) {
+  ++g_stub.calls;
+  check_search_batch(g, sb, kbar, static_cast<const float*>(g_stub.ws));
+  return hipSuccess;
+}
+
+hipError_t launch_search_batched(const Geometry& g, const SearchBatch& sb, const void*, const void* kbar,
+                                 float* mass, hipStream_t) {
+  ++g_stub.calls;
+  check_search_batch(g, sb, kbar, mass);
+  return hipSuccess;
+}
+
+hipError_t launch_select_batched(const Geometry& g, const SearchBatch& sb, const float* mass, int32_t*, int32_t*,
+                                 hipStream_t) {
+  ++g_stub.calls;
+  check_search_batch(g, sb, g_stub.ws, mass);
+  return hipSuccess;
+}
+
 hipError_t launch_union_lists(const Geometry&, const int32_t*, const int32_t*, int32_t*, int32_t*, hipStream_t) {
   ++g_stub.calls;
   return hipSuccess;

@@ -12,5 +12,6 @@ struct StubState {
   long batched_launches = 0;  // head-pair attention launches over several sequences
   long batched_items = 0;
   long single_launches = 0;   // attention launches over one sequence
+  long batched_searches = 0;  // search-stage launches over several sequences
 };
 extern StubState g_stub;

@@ -132,11 +132,12 @@ def test_varlen_and_per_head_checks_on_host():
     p = base(L=300 + 1000 + 128)
     lens = (ctypes.c_int32 * 3)(300, 1000, 128)
     need = lib.rr_workspace_bytes_varlen(ctypes.byref(p), 3, lens)
-    # the searches share the longest sequence's pooled keys and masses; the one attention launch needs
-    # every sequence's V re-layout, then the queue counters
+    # the batched search holds every sequence's pooled keys and masses at once; the one attention launch
+    # needs every sequence's V re-layout, then the queue counters
     al = lambda x: -(-x // 256) * 256
     vt = lambda L: al(-(-L // 128) * 128 * 8 * 128 * 2)
-    assert need == al(63 * 8 * 128 * 2) + al(32 * 8 * 8 * 4) + vt(300) + vt(1000) + vt(128) + 256
+    srch = lambda L: al(-(-L // 16) * 8 * 128 * 2) + al(32 * (-(-L // 128)) ** 2 * 4)
+    assert need == srch(300) + srch(1000) + srch(128) + vt(300) + vt(1000) + vt(128) + 256
     # fp32 (one attention launch per sequence): the largest single sequence decides
     pf = base(L=300 + 1000 + 128, dtype=rr.RR_FP32)
     assert lib.rr_workspace_bytes_varlen(ctypes.byref(pf), 3, lens) == rr.rr_workspace_bytes(base(L=1000, dtype=rr.RR_FP32))
