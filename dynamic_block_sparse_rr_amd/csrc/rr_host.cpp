@@ -182,12 +182,14 @@ rr_status rr_prefill(const rr_problem* p, const void* q, const void* k, const vo
 }
 
 // Packed variable-length batch: the per-sequence problems, validated before
-// anything is enqueued, and the workspace the batch needs. Every search runs
-// on the first part (pooled keys and masses of the longest sequence). With
-// the head-pair kernel the attention of the whole batch is one launch, so
-// every sequence's V re-layout follows (vt_base, in sequence order), then the
-// queue counters (queues); otherwise each sequence's attention reuses the
-// workspace as a single sequence would.
+// anything is enqueued, and the workspace the batch needs. Without the
+// head-pair kernel each sequence is searched and attended in turn and reuses
+// the workspace as a single sequence would (total = the largest single
+// layout). With it, the first part holds the pooled keys and masses of every
+// sequence at once (a batched search) or of the longest one (a sequence run
+// on its own), whichever is larger; every sequence's V re-layout follows
+// (vt_base, in sequence order), then the queue counters (queues). A sequence
+// run on its own uses the single-sequence layout, which lies inside this one.
 struct VarlenWorkspace {
   size_t vt_base, queues, total;
   bool batched;
@@ -255,10 +257,10 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
   Seq seqs_small[64];
   Seq* seqs = n_seq <= 64 ? seqs_small : new (std::nothrow) Seq[n_seq];
   if (!seqs) return RR_ERR_INVALID_ARG;
-  struct Free {
-    Seq *p, *keep;
-    ~Free() {
-      if (p != keep) delete[] p;
+  struct FreeSeqs {  // releases seqs on every return below
+    Seq *heap, *inline_buf;
+    ~FreeSeqs() {
+      if (heap != inline_buf) delete[] heap;
     }
   } free_seqs{seqs, seqs_small};
   {
@@ -305,10 +307,9 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
   // Head-pair attention, longest sequences first: a sequence with at least
   // kVarlenSoloItemsPerCU work items per CU is searched and attended in
   // launches of its own (a single-sequence launch fills the GPU and can
-  // balance its XCDs through the work queues); the others are searched one
-  // after the other and attended together in one launch per group of
-  // kMaxSeqPerLaunch, after one V re-layout launch for the group, each
-  // sequence's work items on a range of their own.
+  // balance its XCDs through the work queues); the others are searched
+  // together and attended together, one launch per kernel per group of
+  // kMaxSeqPerLaunch, each sequence's work on a range of its own.
   std::stable_sort(seqs, seqs + n_seq, [](const Seq& a, const Seq& b) { return a.len > b.len; });
   int ncu = 0;
   hipError_t e = rr::attn_cu_count(st, &ncu);
@@ -366,10 +367,7 @@ rr_status rr_prefill_varlen(const rr_problem* p, int32_t n_seq, const int32_t* s
     int items = 0, tiles = 0;
     for (int m = 0; m < sb.n; ++m) {
       const Seq& sq = seqs[b0 + m];
-      rr_problem pb = *p;
-      pb.L = sq.len;
-      rr::Geometry g;
-      make_geometry(&pb, &g);
+      const rr::Geometry g = geometry(sq);
       sb.item_off[m] = items;
       sb.tile_off[m] = tiles;
       sb.tok_off[m] = (int)sq.tok;
