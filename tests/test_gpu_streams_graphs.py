@@ -136,3 +136,53 @@ def test_decode_graph_replays_match_eager_calls():
             n = int(rc[h])
             assert torch.equal(got[2][h, :n], ci[h, :n])
     say("  decode graph: 3 replays on new queries, each bitwise equal to the eager call")
+
+
+def test_varlen_graph_replays_match_eager_calls():
+    # 17,000 tokens at the 8B shape: a sequence searched and attended in launches of its own;
+    # the three short ones searched and attended together
+    lens = [17000, 3000, 999, 500]
+    shape = dict(Hq=32, Hkv=8)
+
+    def inputs(seed):
+        parts = [make_inputs(Workload(f"vg{b}", L, 32, 8, 128, "bf16", 128, 16, (0.9,), seed + b, "llm", 8))
+                 for b, L in enumerate(lens)]
+        return [torch.cat([x[i] for x in parts]).cuda() for i in range(3)]
+
+    q, k, v = inputs(50)
+    p = rr.problem(sum(lens), shape["Hq"], shape["Hkv"], 128, 16, 128, 0.9, True, "bf16")
+    nbs = [-(-L // 128) for L in lens]
+    rc = torch.empty((sum(32 * n for n in nbs),), dtype=torch.int32, device="cuda")
+    ci = torch.empty((sum(32 * n * n for n in nbs),), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(rr.rr_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
+
+    def run():
+        rr.rr_prefill_varlen(p, lens, q, k, v, out, rc, ci, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        nq, nk, nv = inputs(60 + 10 * rep)
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), rc.clone(), ci.clone())
+        out.fill_(0)
+        rc.fill_(-1)
+        torch.cuda.synchronize()
+        run()
+        torch.cuda.synchronize()
+        assert same(got, (out, rc, ci)), rep
+    say("  varlen graph: 3 replays on new inputs, each bitwise equal to the eager call")
