@@ -208,7 +208,7 @@ static float best_ms(F launch, int reps) {
 
 struct Summary {
   double bf16_reg_1w = 0, bf16_reg_2w = 0, bf16_lds_2w = 0, f32_reg_2w = 0;
-  double bf16_reg_2w_rand = 0, bf16_lds_2w_rand = 0;
+  double bf16_reg_2w_rand = 0, bf16_lds_2w_rand = 0, bf16_lds_1w_rand = 0;
   double copy_GBps = 0, read_GBps = 0;
   double cache_stream_GBps = 0, cache_walk_GBps = 0;
   int ncu = 0, clock_khz = 0;
@@ -227,6 +227,8 @@ static void run_mfma(Summary& s) {
   CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_reg<512, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
   CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<512, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<256, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
   CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_bf16_lds<512, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
@@ -261,6 +263,12 @@ static void run_mfma(Summary& s) {
   printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"one ds_read_b128 A operand per MFMA, pseudo-random "
          "operands\", \"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
          s.bf16_lds_2w_rand);
+  // the same stream from one wave per SIMD (the feed of each MFMA half-step of the ping-pong attention)
+  ms = best_ms([&] { mfma_bf16_lds<256, true><<<grid, 256, kLdsBytes>>>(iters, out); }, 5);
+  s.bf16_lds_1w_rand = rate(f_bf16, 256, ms);
+  printf("{\"probe\": \"mfma_bf16_32x32x16\", \"feed\": \"one ds_read_b128 A operand per MFMA, pseudo-random "
+         "operands\", \"waves_per_simd\": 1, \"TFLOPs\": %.1f}\n",
+         s.bf16_lds_1w_rand);
   ms = best_ms([&] { mfma_f32_reg<512><<<grid, 512, kLdsBytes>>>(iters / 2, out); }, 5);
   s.f32_reg_2w = f_f32 * kAcc * (iters / 2) * (double)grid * 8 / (ms * 1e-3) / 1e12;
   printf("{\"probe\": \"mfma_f32_32x32x2\", \"feed\": \"registers\", \"waves_per_simd\": 2, \"TFLOPs\": %.1f}\n",
@@ -410,11 +418,12 @@ int main(int argc, char** argv) {
   printf("{\"summary\": {\"cus\": %d, \"max_clock_mhz\": %d, \"mfma_bf16_reg_1w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_random_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_random_TFLOPs\": %.1f, "
+         "\"mfma_bf16_lds_1w_random_TFLOPs\": %.1f, "
          "\"mfma_f32_reg_2w_TFLOPs\": %.2f, "
          "\"hbm_copy_GBps\": %.1f, \"hbm_read_GBps\": %.1f, \"cache_stream_GBps\": %.1f, "
          "\"cache_walk_GBps\": %.1f}}\n",
          s.ncu, s.clock_khz / 1000, s.bf16_reg_1w, s.bf16_reg_2w, s.bf16_lds_2w, s.bf16_reg_2w_rand,
-         s.bf16_lds_2w_rand, s.f32_reg_2w, s.copy_GBps,
+         s.bf16_lds_2w_rand, s.bf16_lds_1w_rand, s.f32_reg_2w, s.copy_GBps,
          s.read_GBps, s.cache_stream_GBps, s.cache_walk_GBps);
   return 0;
 }
