@@ -706,6 +706,12 @@ def main():
             if ml > 0:
                 line["roofline"]["peak_lds_fed_random_operands"] = ml
                 line["roofline"]["frac_lds_fed_random_operands"] = round(attn_tflops / ml, 4)
+            # ... and with a softmax-like VALU stream on the same SIMDs, as much VALU work per MFMA as the
+            # attention issues (peak.hip coexec): the rate a kernel doing both can reach on this GPU
+            mv = float(peaks.get("mfma_bf16_lds_random_with_softmax_valu_TFLOPs", 0.0))
+            if mv > 0:
+                line["roofline"]["peak_lds_fed_with_softmax_valu"] = mv
+                line["roofline"]["frac_lds_fed_with_softmax_valu"] = round(attn_tflops / mv, 4)
         line["measured_peaks"] = peaks
     tr = measured_traffic(w.name, tau)
     if tr is not None:

@@ -12,8 +12,10 @@
 // Every rate is the best of several timed repetitions (HIP events). Prints
 // one JSON line per measurement and a last line {"summary": {...}}.
 //   - (chains) the rate of one wave per SIMD with 1, 2, 4 or 8 independent
-//     accumulator chains.
-// Usage: peak [all|mfma|hbm|cache|chains] [L] [Hkv]
+//     accumulator chains;
+//   - (coexec) an LDS-fed MFMA stream beside a softmax-like VALU stream on the
+//     same SIMDs, each alone and both together.
+// Usage: peak [all|mfma|hbm|cache|chains] [L] [Hkv], or peak coexec [valu rounds]
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -130,6 +132,65 @@ __global__ void __launch_bounds__(THREADS) mfma_bf16_lds(int iters, float* out) 
   out[(size_t)blockIdx.x * THREADS + t] = s;
 }
 
+// An LDS-fed MFMA stream (waves 0-3, one per SIMD: one ds_read_b128 A operand
+// per MFMA, four reads in flight, pseudo-random operands) beside a VALU stream
+// like a softmax (waves 4-7: FMA and exp2 over 64 values per lane, viters
+// rounds), in one workgroup per CU. MODE bit 0: the MFMA waves run; bit 1:
+// the VALU waves run. The time of both together against each alone bounds what
+// a kernel that must do both on the same SIMDs can reach.
+template <int MODE>
+__global__ void __launch_bounds__(512) coexec_kernel(int iters, int viters, float* out) {
+  extern __shared__ uint8_t lds[];
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const uint32_t gt = blockIdx.x * 512 + t;
+  for (int i = t; i < kLdsSlots * 64; i += 512) {
+    bf16x8 x;
+    for (int e = 0; e < 8; ++e) x[e] = (__bf16)hash_value(5, (blockIdx.x * kLdsSlots * 64 + i) * 8 + e);
+    *reinterpret_cast<bf16x8*>(lds + (size_t)i * 16) = x;
+  }
+  __syncthreads();
+  float s = 0.0f;
+  if (w < 4) {
+    if (!(MODE & 1)) return;
+    bf16x8 b;
+    for (int e = 0; e < 8; ++e) b[e] = (__bf16)hash_value(2, gt * 8 + e);
+    f32x16 acc[4];
+    for (int n = 0; n < 4; ++n) acc[n] = f32x16{};
+    auto rd = [&](int step) {
+      return *reinterpret_cast<const bf16x8*>(lds + (step & (kLdsSlots - 1)) * 1024 + lane * 16);
+    };
+    bf16x8 ring[4];
+    for (int n = 0; n < 4; ++n) ring[n] = rd(n);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bf16x8 x = ring[n];
+        ring[n] = rd(it * 4 + n + 4);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, b, acc[n], 0, 0, 0);
+      }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    for (int n = 0; n < 4; ++n)
+      for (int v = 0; v < 16; ++v) s += acc[n][v];
+  } else {
+    if (!(MODE & 2)) return;
+    float x[64];
+    for (int e = 0; e < 64; ++e) x[e] = hash_value(3, gt * 64 + e);
+    float m = 0.5f;
+    for (int it = 0; it < viters; ++it) {
+#pragma unroll
+      for (int e = 0; e < 64; ++e) x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], 0.25f, -m));
+      m = x[0] * 0.001f;  // a fixed element: a varying index would put x in scratch memory
+    }
+    for (int e = 0; e < 64; ++e) s += x[e];
+  }
+  out[gt] = s;
+}
+
 // One wave per SIMD, register operands, NACC independent accumulator chains
 // (8 MFMAs per loop trip): how many chains one wave needs to keep the matrix
 // unit busy.
@@ -208,7 +269,7 @@ static float best_ms(F launch, int reps) {
 
 struct Summary {
   double bf16_reg_1w = 0, bf16_reg_2w = 0, bf16_lds_2w = 0, f32_reg_2w = 0;
-  double bf16_reg_2w_rand = 0, bf16_lds_2w_rand = 0, bf16_lds_1w_rand = 0;
+  double bf16_reg_2w_rand = 0, bf16_lds_2w_rand = 0, bf16_lds_1w_rand = 0, bf16_lds_valu = 0;
   double copy_GBps = 0, read_GBps = 0;
   double cache_stream_GBps = 0, cache_walk_GBps = 0;
   int ncu = 0, clock_khz = 0;
@@ -383,6 +444,36 @@ static void run_chains_one(int ncu, float* out) {
          "\"TFLOPs\": %.1f}\n", NACC, tf);
 }
 
+template <int MODE>
+static float coexec_ms(int ncu, float* out, int iters, int viters) {
+  CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&coexec_kernel<MODE>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes));
+  return best_ms([&] { coexec_kernel<MODE><<<ncu * 4, 512, kLdsBytes>>>(iters, viters, out); }, 5);
+}
+
+static double run_coexec(int ncu, int viters) {
+  const int iters = 8192;  // 32,768 MFMAs per MFMA wave
+  float* out = nullptr;
+  CHECK(hipMalloc(&out, (size_t)ncu * 4 * 512 * sizeof(float)));
+  (void)coexec_ms<1>(ncu, out, iters, viters);  // warm-up
+  const float m = coexec_ms<1>(ncu, out, iters, viters);
+  const float v = coexec_ms<2>(ncu, out, iters, viters);
+  const float b = coexec_ms<3>(ncu, out, iters, viters);
+  const double fl = (double)ncu * 4 * 4 * iters * 4 * 32768.0;
+  printf("{\"probe\": \"coexec\", \"valu_rounds\": %d, \"mfma_alone_ms\": %.3f, \"valu_alone_ms\": %.3f, "
+         "\"both_ms\": %.3f, \"valu_to_mfma_time\": %.2f, \"mfma_alone_TFLOPs\": %.1f, \"both_TFLOPs\": %.1f}\n",
+         viters, m, v, b, v / m, fl / (m * 1e-3) / 1e12, fl / (b * 1e-3) / 1e12);
+  CHECK(hipFree(out));
+  return fl / (b * 1e-3) / 1e12;
+}
+
+// VALU rounds of the co-execution probe that match the ping-pong attention's mix:
+// per 64 MFMAs the attention issues about 257 other VALU instructions, 64 of them
+// exp2 (instruction counters of the 128K layer), i.e. 321 FMA-equivalents with
+// exp2 at half rate; 860 rounds give the probe's MFMA waves 107.5 exp2 and 107.5
+// FMA per 64 MFMAs, 322.5 FMA-equivalents.
+constexpr int kAttnValuRounds = 860;
+
 static void run_chains(int ncu) {
   float* out = nullptr;
   CHECK(hipMalloc(&out, (size_t)ncu * 4 * 256 * sizeof(float)));
@@ -398,9 +489,22 @@ int main(int argc, char** argv) {
   const char* what = argc > 1 ? argv[1] : "all";
   const int L = argc > 2 ? atoi(argv[2]) : 131072, H = argc > 3 ? atoi(argv[3]) : 8;
   const bool all = !strcmp(what, "all");
-  if (!all && strcmp(what, "mfma") && strcmp(what, "hbm") && strcmp(what, "cache") && strcmp(what, "chains")) {
-    fprintf(stderr, "usage: peak [all|mfma|hbm|cache|chains] [L] [Hkv]\n");
+  if (!all && strcmp(what, "mfma") && strcmp(what, "hbm") && strcmp(what, "cache") && strcmp(what, "chains") &&
+      strcmp(what, "coexec")) {
+    fprintf(stderr, "usage: peak [all|mfma|hbm|cache|chains|coexec] [L] [Hkv]   (coexec: [valu rounds])\n");
     return 2;
+  }
+  if (!strcmp(what, "coexec")) {
+    int dev0 = 0, ncu0 = 0;
+    CHECK(hipGetDevice(&dev0));
+    CHECK(hipDeviceGetAttribute(&ncu0, hipDeviceAttributeMultiprocessorCount, dev0));
+    const int vr = argc > 2 ? atoi(argv[2]) : 170;
+    if (vr < 1 || vr > 10000) {
+      fprintf(stderr, "peak coexec: valu rounds in [1, 10000]\n");
+      return 2;
+    }
+    run_coexec(ncu0, vr);
+    return 0;
   }
   if (L < 128 || L % 128 != 0 || H < 1 || (long long)L * H > (1ll << 26)) {
     fprintf(stderr, "peak: L must be a positive multiple of 128 and L*Hkv <= 2^26\n");
@@ -411,19 +515,22 @@ int main(int argc, char** argv) {
   CHECK(hipGetDevice(&dev));
   CHECK(hipDeviceGetAttribute(&s.ncu, hipDeviceAttributeMultiprocessorCount, dev));
   CHECK(hipDeviceGetAttribute(&s.clock_khz, hipDeviceAttributeClockRate, dev));
-  if (all || !strcmp(what, "mfma")) run_mfma(s);
+  if (all || !strcmp(what, "mfma")) {
+    run_mfma(s);
+    s.bf16_lds_valu = run_coexec(s.ncu, kAttnValuRounds);
+  }
   if (all || !strcmp(what, "hbm")) run_hbm(s);
   if (!strcmp(what, "cache")) run_cache(s, L, H);
   if (!strcmp(what, "chains")) run_chains(s.ncu);
   printf("{\"summary\": {\"cus\": %d, \"max_clock_mhz\": %d, \"mfma_bf16_reg_1w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_TFLOPs\": %.1f, "
          "\"mfma_bf16_reg_2w_random_TFLOPs\": %.1f, \"mfma_bf16_lds_2w_random_TFLOPs\": %.1f, "
-         "\"mfma_bf16_lds_1w_random_TFLOPs\": %.1f, "
+         "\"mfma_bf16_lds_1w_random_TFLOPs\": %.1f, \"mfma_bf16_lds_random_with_softmax_valu_TFLOPs\": %.1f, "
          "\"mfma_f32_reg_2w_TFLOPs\": %.2f, "
          "\"hbm_copy_GBps\": %.1f, \"hbm_read_GBps\": %.1f, \"cache_stream_GBps\": %.1f, "
          "\"cache_walk_GBps\": %.1f}}\n",
          s.ncu, s.clock_khz / 1000, s.bf16_reg_1w, s.bf16_reg_2w, s.bf16_lds_2w, s.bf16_reg_2w_rand,
-         s.bf16_lds_2w_rand, s.bf16_lds_1w_rand, s.f32_reg_2w, s.copy_GBps,
+         s.bf16_lds_2w_rand, s.bf16_lds_1w_rand, s.bf16_lds_valu, s.f32_reg_2w, s.copy_GBps,
          s.read_GBps, s.cache_stream_GBps, s.cache_walk_GBps);
   return 0;
 }
