@@ -178,3 +178,51 @@ def test_varlen_long_sequence_in_its_own_launch():
     per CU on 256 CUs: that sequence gets a launch of its own, the two short
     ones share one."""
     _varlen_case([17000, 3000, 999], 32, 8, 310)
+
+
+def test_varlen_many_random_lengths_match_single_sequences():
+    """40 sequences of seeded random lengths (1 to 3,000 tokens: one-block and
+    one-token sequences, lengths off the block and the stride): two shared
+    launch groups (32 + 8) for the search and the attention. Every sequence's
+    lists and output equal the same sequence run alone, bit for bit; the lists
+    of every sequence and the outputs of every fifth sequence against the oracle."""
+    rng = np.random.default_rng(777)
+    lens = [int(x) for x in rng.integers(1, 3001, 40)]
+    lens[3], lens[17], lens[30] = 1, 128, 129  # one token, one whole block, one block and a token
+    Hq, Hkv = 8, 2
+    ws_ = [Workload(f"r{b}", L, Hq, Hkv, 128, "bf16", 128, 16, (0.9,), 900 + b, "llm" if L >= 64 else "gauss", 8)
+           for b, L in enumerate(lens)]  # the 8B-shaped recipe needs more tokens than its 8 stripes
+    parts = [make_inputs(w_) for w_ in ws_]
+    q = torch.cat([p_[0] for p_ in parts]).cuda()
+    k = torch.cat([p_[1] for p_ in parts]).cuda()
+    v = torch.cat([p_[2] for p_ in parts]).cuda()
+    p = rr.problem(sum(lens), Hq, Hkv, 128, 16, 128, 0.9, True, "bf16")
+    nbs = [-(-L // 128) for L in lens]
+    rc = torch.full((sum(Hq * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
+    ci = torch.full((sum(Hq * n * n for n in nbs),), -1, dtype=torch.int32, device="cuda")
+    out = torch.full_like(q, float("nan"))
+    ws = torch.empty(rr.rr_workspace_bytes_varlen(p, lens), dtype=torch.uint8, device="cuda")
+    rr.rr_prefill_varlen(p, lens, q, k, v, out, rc, ci, ws)
+    torch.cuda.synchronize()
+    rc, ci, out = rc.cpu().numpy(), ci.cpu().numpy(), out.float().cpu().numpy()
+    tok = roff = coff = 0
+    for b, L in enumerate(lens):
+        nb = nbs[b]
+        o1, rc1, ci1 = DeviceCase(ws_[b], 0.9, inputs=parts[b]).prefill()
+        rcb = rc[roff:roff + Hq * nb].reshape(Hq, nb)
+        cib = ci[coff:coff + Hq * nb * nb].reshape(Hq, nb, nb)
+        np.testing.assert_array_equal(rcb, rc1)
+        for h in range(Hq):
+            for i in range(nb):
+                np.testing.assert_array_equal(cib[h, i, :rcb[h, i]], ci1[h, i, :rc1[h, i]])
+        np.testing.assert_array_equal(out[tok:tok + L], o1)
+        orc = oracle.search(parts[b][0], parts[b][1], S=16, B=128, tau=0.9, round_bf16=True)
+        assert checker.classify(rcb, cib, orc, 0.9)["fail"] == 0, b
+        if b % 5 == 0:
+            want = oracle.attention(parts[b][0], parts[b][1], parts[b][2], rcb, cib, B=128)
+            mx, mean = checker.output_errors(out[tok:tok + L], want)
+            assert mx <= 2e-2 and mean <= 2e-3, (b, mx, mean)
+        tok += L
+        roff += Hq * nb
+        coff += Hq * nb * nb
+    say(f"  varlen 40 random lengths ({min(lens)}..{max(lens)}): lists and outputs bitwise equal to single runs")
