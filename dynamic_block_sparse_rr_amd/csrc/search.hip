@@ -415,17 +415,31 @@ __global__ void __launch_bounds__(256) search_kernel(const T* __restrict__ q_all
 
 // ------------------------------------------------------------------ selection
 
-// Sum over the 64 lanes in one fixed order (xor butterfly), taken from lane 0
-// so every lane holds the same value.
+// Sum over the 64 lanes in one fixed order (pairs of lanes, then of 2, 4, 8,
+// 16 and 32 lanes, by DPP and permlane moves: no LDS round trip), taken from
+// lane 0 so every lane holds the same value.
+__device__ __forceinline__ float lanes16_swap_add(float x) {  // x + the value of the lane 16 apart
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 __device__ __forceinline__ float wave_total(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  x = add_halves(lanes16_swap_add(sum_lane_groups<16>(x)));
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x140>(x));
+  {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
 }
 
