@@ -993,170 +993,246 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
 
 // ------------------------------------------------------------------ fp32 attention
 
-// float32 path on the fp32 matrix cores (v_mfma_f32_32x32x2f32). A workgroup
-// of f32_waves(D) waves (8 at d = 64, 4 at d = 128, as LDS allows) serves one
-// query head and one tile of 32 queries; wave w takes entries w, w + waves,
-// ... of the row's block list, walks each
-// selected block in 32-key subtiles staged in its own LDS area, and keeps
-// its own running maximum, sum and O; the waves' partial results are merged
-// at the end (each part rescaled to the common maximum). Per subtile:
-//   S^T = K Q^T, D/2 MFMAs: A = K (32 keys x 2 channels, one LDS float per
-//     lane, rows padded to D+1 floats so the 32 keys of a read fall in
-//     distinct banks), B = Q^T (the lane's query, two channels: registers);
-//     lane (query n, half hf) then holds keys 8*(v/4) + 4*hf + v%4, v < 16;
-//   online softmax in base 2 on those 16 scores (one cross-half exchange);
-//   O^T += Vt P^T, 16 MFMAs per 32 channels: MFMA v pairs key 8*(v/4) + v%4
-//     (lane half 0) with key 8*(v/4) + 4 + v%4 (half 1), exactly the keys the
-//     lane's P register v holds, so P is the B operand as it stands, and A
-//     reads V[that key][the lane's channel] from LDS.
-__host__ __device__ constexpr int f32_waves(int D) { return D == 64 ? 8 : 4; }
+// float32 path on the fp32 matrix cores (v_mfma_f32_16x16x4f32). A workgroup of
+// f32_waves(D) waves serves one query head and one tile of 16 queries (so even a
+// 1K-token layer spreads over a few hundred workgroups); the row's selected
+// blocks are cut into 16-key subtiles and wave w takes subtiles w, w + waves,
+// ... Lane (i = lane % 16, grp = lane / 16) keeps its own running maximum, sum
+// and O for query i; the waves' parts are merged at the end (each rescaled to
+// the common maximum). The operands come from global memory straight into
+// registers in the matrix layout, the next subtile's while the current one is
+// computed; no staging through LDS:
+//   S^T = K Q^T, D/4 MFMAs: step s takes channel grp * D/4 + s from every lane
+//     group (the sum over channels may run in any order), so A = K[key i]
+//     and B = Q[query i] are each D/4 contiguous floats of the lane; the lane
+//     then holds the scores of keys 4 grp + r, r < 4, for query i;
+//   online softmax in base 2 on those 4 scores (maximum across the 4 groups);
+//   O^T += V^T P^T, 4 * D/16 MFMAs: step r pairs key 4 grp + r across the
+//     groups, exactly the key of the lane's P register r, so P is the B
+//     operand as it stands; row i of output tile c is channel i * D/16 + c,
+//     so A = V[key 4 grp + r][i * D/16 + c], D/16 contiguous floats per key.
+// After the loop the lane holds O^T for channels grp * D/4 ... grp * D/4 +
+// D/4 - 1 of query i, in order (4 rows per output tile, D/16 tiles).
+// Waves per workgroup: 8, two per SIMD (16 at d = 64, four per SIMD within
+// 128 VGPRs, ran the 1K-token layer 13% slower: twice the parts to merge).
+__host__ __device__ constexpr int f32_waves(int) { return 8; }
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The larger of x and the value of the lane 16 (32) apart, by one permlane
+// swap (no LDS round trip).
+__device__ __forceinline__ float max_lane16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float max_lane32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+// x plus the value of the lane 16 (32) apart
+__device__ __forceinline__ float add_lane16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+__device__ __forceinline__ float add_lane32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 
 template <int D>
 struct F32Lds {
-  static constexpr int F32_WAVES = f32_waves(D);
-  static constexpr int KP = D + 1;                 // padded row of a staged K or V subtile (floats)
-  static constexpr int WAVE = 2 * 32 * KP;         // floats per wave: K and V subtiles
-  static constexpr int MERGE = 32 * D + 64;        // floats per wave for the merge: O^T [D][32], m, l
-  static constexpr int PER_WAVE = WAVE > MERGE ? WAVE : MERGE;
-  static constexpr size_t BYTES = (size_t)F32_WAVES * PER_WAVE * sizeof(float);
+  static constexpr int OP = D + 4;                 // padded row of a wave's O part (floats)
+  static constexpr int PER_WAVE = 16 * OP + 32;    // O [16][OP], maximum [16], sum [16]
+  static constexpr size_t BYTES = (size_t)f32_waves(D) * PER_WAVE * sizeof(float);
 };
 
 template <int D, int BLK>
 __global__ void __launch_bounds__(f32_waves(D) * 64) attn_f32_kernel(const float* __restrict__ q,
-                                                                  const float* __restrict__ k,
-                                                                  const float* __restrict__ v,
-                                                                  const int32_t* __restrict__ row_count,
-                                                                  const int32_t* __restrict__ col_idx,
-                                                                  float* __restrict__ out, int Hq, int Hkv, int nb,
-                                                                  int causal, float cscale, int L, int ntiles) {
+                                                                 const float* __restrict__ k,
+                                                                 const float* __restrict__ v,
+                                                                 const int32_t* __restrict__ row_count,
+                                                                 const int32_t* __restrict__ col_idx,
+                                                                 float* __restrict__ out, int Hq, int Hkv, int nb,
+                                                                 int causal, float cscale, int L, int ntiles) {
   typedef F32Lds<D> Lds;
-  constexpr int KP = Lds::KP;
-  constexpr int F32_WAVES = Lds::F32_WAVES;
+  constexpr int KQ = D / 4;    // channels of a lane in S^T (one quarter)
+  constexpr int VC = D / 16;   // channels of a lane per key in O^T += V^T P^T, and output tiles
+  constexpr int NST = BLK / 16;
+  constexpr int W = f32_waves(D);
   extern __shared__ float smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n32 = lane & 31, half = lane >> 5;
+  const int li = lane & 15, grp = lane >> 4;
   // longest rows first: query tiles in decreasing order, heads adjacent
   const int qt = ntiles - 1 - (int)blockIdx.x / Hq;
   const int h = (int)blockIdx.x % Hq;
   const int g = h / (Hq / Hkv);
-  const int i = qt * 32 / BLK;                  // query block of this tile
-  const int x = qt * 32 + n32;                  // this lane's query
-  float* ks = smem + wave * Lds::PER_WAVE;      // K subtile [32][KP]
-  float* vs = ks + 32 * KP;                     // V subtile [32][KP]
+  const int q0 = qt * 16;
+  const int i = q0 / BLK;        // query block of this tile
+  const int x = q0 + li;         // this lane's query
 
-  float qf[D / 2];  // B operand of step kk: channel 2*kk + half of the lane's query
+  // queries past L (the last tile of a ragged layer) read row L - 1, replaced
+  // by zeros after the load (a load under a branch would leave it in flight
+  // into the loop, where the wait counts then cover every load)
+  float qf[KQ];
+  {
+    const f32x4* src = reinterpret_cast<const f32x4*>(q + ((size_t)min(x, L - 1) * Hq + h) * D + grp * KQ);
+    const bool qin = x < L;
 #pragma unroll
-  for (int kk = 0; kk < D / 2; ++kk) qf[kk] = x < L ? q[((size_t)x * Hq + h) * D + 2 * kk + half] : 0.0f;
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) oacc[t] = f32x16{};
-  float mrow = -INFINITY, lrow = 0.0f;
+    for (int c = 0; c < KQ / 4; ++c) {
+      f32x4 t = src[c];
+      if (!qin) t = f32x4{0.f, 0.f, 0.f, 0.f};
+      qf[4 * c] = t[0]; qf[4 * c + 1] = t[1]; qf[4 * c + 2] = t[2]; qf[4 * c + 3] = t[3];
+    }
+  }
 
   const size_t row = (size_t)h * nb + i;
   const int cnt = min(max(row_count[row], 0), nb);
   const int32_t* lst = col_idx + row * nb;
   const int jmax = causal ? i : nb - 1;
-  for (int c = wave; c < cnt; c += F32_WAVES) {
-    const int j = min(max(lst[c], 0), jmax);
-    for (int st = 0; st < BLK / 32; ++st) {
-      const int key0 = j * BLK + st * 32;  // first key of the subtile
-      // skip subtiles with no visible key for any query of the tile (wave-uniform)
-      if (key0 >= L) break;
-      if (causal && key0 > qt * 32 + 31) break;
-      // stage K and V rows key0 .. key0+31 (zeros past L)
-      for (int n = lane; n < 32 * D / 4; n += 64) {
-        const int r = n / (D / 4), c4 = n % (D / 4);
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-        if (key0 + r < L) {
-          const size_t src = ((size_t)(key0 + r) * Hkv + g) * D + c4 * 4;
-          kv = *reinterpret_cast<const float4*>(k + src);
-          vv = *reinterpret_cast<const float4*>(v + src);
-        }
-        float* kd = ks + r * KP + c4 * 4;
-        float* vd = vs + r * KP + c4 * 4;
-        kd[0] = kv.x; kd[1] = kv.y; kd[2] = kv.z; kd[3] = kv.w;
-        vd[0] = vv.x; vd[1] = vv.y; vd[2] = vv.z; vd[3] = vv.w;
-      }
-      // this wave's LDS writes are done before any of its lanes reads
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      f32x16 sacc = f32x16{};
+  const int total = cnt * NST;  // subtiles of the row's blocks
+  const int qlast = min(q0 + 15, L - 1);
+  const int klim = causal ? min(x, L - 1) : L - 1;  // last key the lane's query sees
+
+  // first key of subtile t of the row (any t: past the list it reads entry 0,
+  // unused); t is the same in every lane, and so is the key
+  auto key_of = [&](int t) {
+    const int c = t < total ? t / NST : 0;
+    return __builtin_amdgcn_readfirstlane(min(max(lst[c], 0), jmax) * BLK + (t % NST) * 16);
+  };
+  // K rows key0 + li (quarter grp) and V rows key0 + 4 grp + r (D/16 channels)
+  // through buffer descriptors that start at row key0 and end at row L or 16
+  // rows on, so rows past L read as zeros with no branch and no select on the
+  // loaded values: nothing waits for the loads until the subtile is computed.
+  // A subtile past the row's list gets an empty range: its loads are issued
+  // all the same, with no memory access, since a load under a branch would make
+  // every later wait cover the loads of both sides.
+  const uint32_t rowb = (uint32_t)(Hkv * D * 4);
+  auto load = [&](int t, int key0, float (&kr)[KQ], float (&vr)[4][VC]) {
+    const size_t base = ((size_t)key0 * Hkv + g) * D;
+    // the range ends where row key0 + rows begins (rows = the subtile's keys
+    // before L; 32-bit scalar arithmetic): every load of a row below it lies
+    // inside, every load of a row past it outside
+    const int rows = t < total ? min(L - key0, 16) : 0;
+    const uint32_t nbytes = rows <= 0 ? 0u : (uint32_t)rows * rowb - (uint32_t)(g * D * 4);
+    const __amdgpu_buffer_rsrc_t kr_rs = tile_rsrc(reinterpret_cast<const uint8_t*>(k + base), nbytes);
+    const __amdgpu_buffer_rsrc_t vr_rs = tile_rsrc(reinterpret_cast<const uint8_t*>(v + base), nbytes);
+    const uint32_t koff = li * rowb + grp * KQ * 4;
 #pragma unroll
-      for (int kk = 0; kk < D / 2; ++kk)
-        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[n32 * KP + 2 * kk + half], qf[kk], sacc, 0, 0, 0);
-      // keys past the lane's query (causal) or past L are masked
-      const int klim = min(causal ? x : L - 1, L - 1);
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = key0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        if (key > klim) sacc[e] = -INFINITY;
-        tmax = fmaxf(tmax, sacc[e]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrow, tmax * cscale);
-      const float mref = mnew == -INFINITY ? 0.0f : mnew;  // a row with nothing visible yet stays at zero
-      const float alpha = exp2_approx(mrow - mref);
-      lrow *= alpha;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
-      mrow = mnew;
-      float pv[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        pv[e] = exp2_approx(__builtin_fmaf(sacc[e], cscale, -mref));
-        lrow += pv[e];
-      }
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = 8 * (e >> 2) + 4 * half + (e & 3);
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * KP + t * 32 + n32], pv[e], oacc[t], 0, 0, 0);
-        }
-      // every lane's reads of this subtile have returned before the next one is staged
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    for (int c = 0; c < KQ / 4; ++c) {
+      const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr_rs, koff + 16 * c, 0, 0));
+      kr[4 * c] = t[0]; kr[4 * c + 1] = t[1]; kr[4 * c + 2] = t[2]; kr[4 * c + 3] = t[3];
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t voff = (4 * grp + r) * rowb + li * VC * 4;
+#pragma unroll
+      for (int c = 0; c < VC / 4; ++c) {
+        const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr_rs, voff + 16 * c, 0, 0));
+        vr[r][4 * c] = t[0]; vr[r][4 * c + 1] = t[1]; vr[r][4 * c + 2] = t[2]; vr[r][4 * c + 3] = t[3];
+      }
+    }
+  };
+
+  f32x4 oacc[VC];
+#pragma unroll
+  for (int c = 0; c < VC; ++c) oacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow = -INFINITY, lrow = 0.0f;
+
+  // one subtile: scores, online softmax, O^T += V^T P^T
+  auto compute = [&](int key0, const float (&kr)[KQ], const float (&vr)[4][VC]) {
+    // subtiles with no key visible to any query of the tile are skipped (wave-uniform)
+    if (key0 >= L || (causal && key0 > qlast)) return;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KQ; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[s], qf[s], sacc, 0, 0, 0);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (key0 + 4 * grp + r > klim) sacc[r] = -INFINITY;
+      tmax = fmaxf(tmax, sacc[r]);
+    }
+    tmax = max_lane32(max_lane16(tmax));
+    const float mnew = fmaxf(mrow, tmax * cscale);
+    const float mref = mnew == -INFINITY ? 0.0f : mnew;  // a query with nothing visible yet stays at zero
+    const float alpha = exp2_approx(mrow - mref);
+    lrow *= alpha;
+#pragma unroll
+    for (int c = 0; c < VC; ++c) oacc[c] *= alpha;
+    mrow = mnew;
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pv[r] = exp2_approx(__builtin_fmaf(sacc[r], cscale, -mref));
+      lrow += pv[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < VC; ++c) oacc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[r][c], pv[r], oacc[c], 0, 0, 0);
+  };
+
+  // Two register sets in turn: while one subtile is computed the next one's
+  // K and V are in flight, and the list entry of the one after that.
+  float ka[KQ], va[4][VC], kb[KQ], vb[4][VC];
+  int t = __builtin_amdgcn_readfirstlane(wave);
+  int keya = key_of(t);
+  int keyb = key_of(t + W);
+  load(t, keya, ka, va);
+  while (t < total) {
+    load(t + W, keyb, kb, vb);
+    const int keyc = key_of(t + 2 * W);
+    compute(keya, ka, va);
+    t += W;
+    if (t >= total) break;
+    load(t + W, keyc, ka, va);
+    const int keyd = key_of(t + 2 * W);
+    compute(keyb, kb, vb);
+    t += W;
+    keya = keyc;  // set A now holds subtile t
+    keyb = keyd;
   }
 
-  // merge the waves' parts: O^T [D][32], the maximum and the sum per query
-  __syncthreads();  // every wave is done with its K/V area
+  // merge the waves' parts: O [16][OP], the maximum and the sum per query
   float* ob = smem + wave * Lds::PER_WAVE;
+  {
+    // output tile c, row 4 grp + rr is channel (4 grp + rr) * VC + c
+    float* dst = ob + li * Lds::OP + grp * KQ;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+    for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ob[(t * 32 + 8 * (e >> 2) + 4 * half + (e & 3)) * 32 + n32] = oacc[t][e];
-  const float ltot = lrow + __shfl_xor(lrow, 32);
-  if (half == 0) {
-    ob[32 * D + n32] = mrow;
-    ob[32 * D + 32 + n32] = ltot;
+      for (int c = 0; c < VC; ++c) dst[rr * VC + c] = oacc[c][rr];
+  }
+  const float ltot = add_lane32(add_lane16(lrow));
+  if (grp == 0) {
+    ob[16 * Lds::OP + li] = mrow;
+    ob[16 * Lds::OP + 16 + li] = ltot;
   }
   __syncthreads();
-  constexpr int TPQ = F32_WAVES * 64 / 32;  // threads per query
+  constexpr int TPQ = W * 64 / 16;  // threads per query
+  constexpr int CPT = D / TPQ;              // channels per thread
+  static_assert(CPT >= 1 && D % TPQ == 0, "channels split evenly over a query's threads");
   const int qq = tid / TPQ, part = tid % TPQ;
-  const int xo = qt * 32 + qq;
-  float mw[F32_WAVES], m = -INFINITY;
+  const int xo = q0 + qq;
+  float mw[W], m = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < F32_WAVES; ++w) {
-    mw[w] = smem[w * Lds::PER_WAVE + 32 * D + qq];
+  for (int w = 0; w < W; ++w) {
+    mw[w] = smem[w * Lds::PER_WAVE + 16 * Lds::OP + qq];
     m = fmaxf(m, mw[w]);
   }
   const float mr = m == -INFINITY ? 0.0f : m;
-  float aw[F32_WAVES], l = 0.0f;
+  float aw[W], l = 0.0f;
 #pragma unroll
-  for (int w = 0; w < F32_WAVES; ++w) {
+  for (int w = 0; w < W; ++w) {
     aw[w] = exp2_approx(mw[w] - mr);
-    l += aw[w] * smem[w * Lds::PER_WAVE + 32 * D + 32 + qq];
+    l += aw[w] * smem[w * Lds::PER_WAVE + 16 * Lds::OP + 16 + qq];
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   if (xo >= L) return;
-  constexpr int CPT = D / TPQ;  // channels per thread
 #pragma unroll
   for (int e = 0; e < CPT; ++e) {
     const int ch = part * CPT + e;
     float o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < F32_WAVES; ++w) o += aw[w] * smem[w * Lds::PER_WAVE + ch * 32 + qq];
+    for (int w = 0; w < W; ++w) o += aw[w] * smem[w * Lds::PER_WAVE + qq * Lds::OP + ch];
     out[((size_t)xo * Hq + h) * D + ch] = o * inv;
   }
 }
@@ -1288,7 +1364,7 @@ hipError_t launch_attention(const Geometry& g, const void* q, const void* k, con
                                                                  g.L, ntiles);                    \
     return hipGetLastError();                                                                     \
   }
-  const int ntiles = (g.L + 31) / 32;
+  const int ntiles = (g.L + 15) / 16;
   const dim3 f32grid((unsigned)(g.Hq * ntiles));
   RR_F32_CASE(128, 128)
   RR_F32_CASE(128, 64)
