@@ -33,6 +33,9 @@ RAGGED = [
     g("mha_b128_tail60", 700, 2, 2, 128, 16, 128, "bf16"),
     g("fp32_tail52", 500, 2, 1, 64, 8, 64, "fp32", kind="tiny"),
     g("fp32_noncausal_tail52", 500, 2, 1, 64, 8, 64, "fp32", causal=False),
+    g("fp32_gqa_tail52", 500, 4, 2, 64, 8, 64, "fp32"),                        # KV head 1's rows end mid-tensor
+    g("fp32_d128_b128_noncausal_tail44", 300, 4, 2, 128, 16, 128, "fp32", causal=False),  # 12-key last subtile
+    g("fp32_seven_tokens", 7, 2, 2, 64, 8, 64, "fp32"),                        # one tile, one short subtile
     g("single_short_block", 50, 4, 2, 64, 8, 64, "bf16"),                      # nb = 1
     g("one_token", 1, 4, 2, 128, 16, 128, "bf16"),                              # L = 1: one key, one stride
     g("two_tokens_noncausal", 2, 4, 2, 128, 16, 128, "bf16", causal=False),
