@@ -488,9 +488,17 @@ __device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, __amdgpu_bu
 }
 
 // Online softmax of one key block for one wave, in base 2 with the scale
-// folded into cscale: running maximum and sum updated, O rescaled when the
-// maximum grew, P rounded to bf16 in the B-operand layout of O^T += Vt P^T.
-// MASK: keys with index > klim inside the block get probability zero.
+// folded into cscale. The probabilities are first taken against the current
+// reference mrow (the largest scaled score seen when it last moved) without
+// looking for the block's maximum: only when the block's sum for some query
+// exceeds kSumLimit (or is not finite, as on a lane's first block, where the
+// reference is the -1e30 sentinel) does the block take the maximum, move the
+// reference, rescale O and the sum, and recompute. Probabilities therefore
+// stay below kSumLimit, far inside the range of bf16 and fp32. P is rounded to
+// bf16 in the B-operand layout of O^T += Vt P^T. MASK: keys with index > klim
+// inside the block get probability zero.
+constexpr float kSumLimit = 65536.0f;
+constexpr float kRefStart = -1e30f;  // reference before any visible key
 template <int D, int BLK, bool MASK>
 __device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (&sacc)[BLK / 32],
                                              f32x16 (&oacc)[D / 32], float& mrow, float& lrow,
@@ -506,43 +514,53 @@ __device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (
         if (key > klim) sacc[mt][v] = -INFINITY;
       }
   }
-  float tmax = -INFINITY;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // P in bf16 (B operand of O^T += Vt P^T) against reference m, and the sum
+  // of exactly the rounded values the MFMA multiplies, two at a time
+  auto probs = [&](float m) __attribute__((always_inline)) {
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+      for (int p2 = 0; p2 < 2; ++p2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -m));
+          const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -m));
+          w[e] = pack_bf16x2(p0, p1);
+          ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
+        }
+        pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+      }
+    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  float tot = probs(mrow);
+  float both;
   {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+    both = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  const float mnew = fmaxf(mrow, tmax * cx.cscale);
-  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
+  if (__builtin_amdgcn_ballot_w64(!(both <= kSumLimit)) != 0) {  // some reference moves
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mnew = fmaxf(mrow, tmax * cx.cscale);
     const float alpha = exp2_approx(mrow - mnew);
     lrow *= alpha;
 #pragma unroll
     for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+    mrow = mnew;
+    tot = probs(mrow);
   }
-  mrow = mnew;
-  // P in bf16 (B operand of O^T += Vt P^T); the row sum adds exactly the
-  // rounded values the MFMA multiplies, two at a time
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
-        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
-        w[e] = pack_bf16x2(p0, p1);
-        ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
-      }
-      pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
-    }
-  }
-  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  lrow += tot;
 }
 
 // Rows (of n) after which the KV head an XCD serves moves on by one: each XCD
@@ -866,7 +884,7 @@ __global__ void __launch_bounds__(4 * BLK) __attribute__((amdgpu_waves_per_eu(2,
     f32x16 oacc[C::NT];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
-    float mrow = -INFINITY, lrow = 0.0f;
+    float mrow = kRefStart, lrow = 0.0f;
     f32x16 sacc[MT];
     bf16x8 pf[MT][2];
 #pragma unroll
