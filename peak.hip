@@ -468,11 +468,11 @@ static double run_coexec(int ncu, int viters) {
 }
 
 // VALU rounds of the co-execution probe that match the ping-pong attention's mix:
-// per 64 MFMAs the attention issues about 257 other VALU instructions, 64 of them
-// exp2 (instruction counters of the 128K layer), i.e. 321 FMA-equivalents with
-// exp2 at half rate; 860 rounds give the probe's MFMA waves 107.5 exp2 and 107.5
-// FMA per 64 MFMAs, 322.5 FMA-equivalents.
-constexpr int kAttnValuRounds = 860;
+// per 64 MFMAs the attention issues about 217 other VALU instructions, 64 of them
+// exp2 (instruction counters of the 128K layer), i.e. 281 FMA-equivalents with
+// exp2 at half rate; 750 rounds give the probe's MFMA waves 93.75 exp2 and 93.75
+// FMA per 64 MFMAs, 281.25 FMA-equivalents.
+constexpr int kAttnValuRounds = 750;
 
 static void run_chains(int ncu) {
   float* out = nullptr;
