@@ -614,7 +614,7 @@ __global__ void __launch_bounds__(256) union_lists_kernel(const int32_t* __restr
       ++pos;
     }
   }
-  if (threadIdx.x < G) out_count[(size_t)(g * G + threadIdx.x) * nb + i] = (int32_t)total;
+  if ((int)threadIdx.x < G) out_count[(size_t)(g * G + threadIdx.x) * nb + i] = (int32_t)total;
 }
 
 // Decode step: per query head, the block masses from the scores' chunk
