@@ -67,6 +67,69 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// Online softmax of one key block for one wave, in base 2 with the scale
+// folded into cscale (the score tiles of S^T = K Q^T: the lane's column is its
+// query, rows are keys). The probabilities are first taken against the current
+// reference mrow (the largest scaled score seen when it last moved) without
+// looking for the block's maximum: only when the block's sum for some query
+// exceeds kSumLimit (or is not finite, as on a lane's first block, where the
+// reference is the kRefStart sentinel) does the block take the maximum, move
+// the reference, rescale O and the sum, and recompute. Probabilities therefore
+// stay below kSumLimit, far inside the range of bf16 and fp32. P is rounded to
+// bf16 in the B-operand layout of O^T += Vt P^T, and the row sum adds exactly
+// the rounded values the MFMA multiplies.
+constexpr float kSumLimit = 65536.0f;
+constexpr float kRefStart = -1e30f;  // reference before any visible key
+template <int MT, int NT>
+__device__ __forceinline__ void ref_softmax(float cscale, f32x16 (&sacc)[MT], f32x16 (&oacc)[NT], float& mrow,
+                                            float& lrow, bf16x8 (&pf)[MT][2]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto probs = [&](float m) __attribute__((always_inline)) {
+    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cscale, -m));
+          const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cscale, -m));
+          w[e] = pack_bf16x2(p0, p1);
+          ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
+        }
+        pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+      }
+    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+  float tot = probs(mrow);
+  float both;  // the query's block sum: the two lane halves hold different keys
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
+    both = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (__builtin_amdgcn_ballot_w64(!(both <= kSumLimit)) != 0) {  // some reference moves
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float mnew = fmaxf(mrow, tmax * cscale);
+    const float alpha = exp2_approx(mrow - mnew);
+    lrow *= alpha;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
+    mrow = mnew;
+    tot = probs(mrow);
+  }
+  lrow += tot;
+}
+
 // Position p (0..15) inside a 16-key group of a Vt row holds key key_of_pos(p)
 // of that group. This matches the order in which a lane holds its
 // probabilities after S^T = K Q^T (lane half hf, register v: key 8*(v/4) +
@@ -247,7 +310,7 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (has_next) copy_tile<D, BLK, AttnCtx<D, BLK>::KCH>(cx, next_k, cx.koff, cx.kstep, cx.lds_k);
 
-  // online softmax in base 2 (scale folded into cscale)
+  // online softmax against the reference (ref_softmax)
   if (masked) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -257,41 +320,8 @@ __device__ __forceinline__ void attn_tile(const AttnCtx<D, BLK>& cx, const bf16x
         if (key > klim) sacc[mt][v] = -INFINITY;
       }
   }
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-    tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-  }
-  const float mnew = fmaxf(mrow, tmax * cx.cscale);
-  if (__builtin_amdgcn_ballot_w64(mnew > mrow) != 0) {  // some row max grew: rescale
-    const float alpha = exp2_approx(mrow - mnew);
-    lrow *= alpha;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-  }
-  mrow = mnew;
-  float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   bf16x8 pf[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -mnew));
-        const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -mnew));
-        ps[e] += p0 + p1;
-        w[e] = pack_bf16x2(p0, p1);
-      }
-      pf[mt][p2] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-  lrow += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  ref_softmax(cx.cscale, sacc, oacc, mrow, lrow, pf);
 
   // V of this block has landed (the next block's K may still be in flight)
   if (has_next)
@@ -393,7 +423,7 @@ __global__ void __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2,
   f32x16 oacc[C::NT];
 #pragma unroll
   for (int t = 0; t < C::NT; ++t) oacc[t] = f32x16{};
-  float mrow = -INFINITY, lrow = 0.0f;
+  float mrow = kRefStart, lrow = 0.0f;
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // queries are in registers
   int j = cnt > 0 ? min(max(lst[0], 0), jmax) : 0;
@@ -487,24 +517,13 @@ __device__ __forceinline__ void pair_copy(const PairCtx<D, BLK>& cx, __amdgpu_bu
         16, (int)(n * step + (off ^ (((n * RPC) & (CH - 1)) << 4))), 0, 0, 0);
 }
 
-// Online softmax of one key block for one wave, in base 2 with the scale
-// folded into cscale. The probabilities are first taken against the current
-// reference mrow (the largest scaled score seen when it last moved) without
-// looking for the block's maximum: only when the block's sum for some query
-// exceeds kSumLimit (or is not finite, as on a lane's first block, where the
-// reference is the -1e30 sentinel) does the block take the maximum, move the
-// reference, rescale O and the sum, and recompute. Probabilities therefore
-// stay below kSumLimit, far inside the range of bf16 and fp32. P is rounded to
-// bf16 in the B-operand layout of O^T += Vt P^T. MASK: keys with index > klim
-// inside the block get probability zero.
-constexpr float kSumLimit = 65536.0f;
-constexpr float kRefStart = -1e30f;  // reference before any visible key
+// Online softmax of one key block for one wave of a head pair (ref_softmax).
+// MASK: keys with index > klim inside the block get probability zero.
 template <int D, int BLK, bool MASK>
 __device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (&sacc)[BLK / 32],
                                              f32x16 (&oacc)[D / 32], float& mrow, float& lrow,
                                              bf16x8 (&pf)[BLK / 32][2], int klim) {
   constexpr int MT = BLK / 32;
-  constexpr int NT = D / 32;
   if (MASK) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -514,53 +533,7 @@ __device__ __forceinline__ void pair_softmax(const PairCtx<D, BLK>& cx, f32x16 (
         if (key > klim) sacc[mt][v] = -INFINITY;
       }
   }
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // P in bf16 (B operand of O^T += Vt P^T) against reference m, and the sum
-  // of exactly the rounded values the MFMA multiplies, two at a time
-  auto probs = [&](float m) __attribute__((always_inline)) {
-    float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e], cx.cscale, -m));
-          const float p1 = exp2_approx(__builtin_fmaf(sacc[mt][8 * p2 + 2 * e + 1], cx.cscale, -m));
-          w[e] = pack_bf16x2(p0, p1);
-          ps[e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ps[e], false);
-        }
-        pf[mt][p2] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
-      }
-    }
-    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
-  };
-  float tot = probs(mrow);
-  float both;
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tot), __float_as_uint(tot), false, false);
-    both = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  if (__builtin_amdgcn_ballot_w64(!(both <= kSumLimit)) != 0) {  // some reference moves
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const float mnew = fmaxf(mrow, tmax * cx.cscale);
-    const float alpha = exp2_approx(mrow - mnew);
-    lrow *= alpha;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) oacc[t] *= alpha;
-    mrow = mnew;
-    tot = probs(mrow);
-  }
-  lrow += tot;
+  ref_softmax(cx.cscale, sacc, oacc, mrow, lrow, pf);
 }
 
 // Rows (of n) after which the KV head an XCD serves moves on by one: each XCD
