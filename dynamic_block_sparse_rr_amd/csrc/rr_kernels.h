@@ -82,7 +82,7 @@ struct SeqBatch {
 // attention's work queues (one per XCD); launch_transpose_v zeroes them, so
 // the two run in this order on one stream, one pair per call at a time.
 constexpr int kAttnQueues = 8;
-bool attn_pair_shape(const Geometry& g);  // bf16, B = 128, two or more query heads per KV head
+bool attn_pair_shape(const Geometry& g);  // bf16 with B = 128: the head-pair kernel
 int attn_items(const Geometry& g);        // work items of one sequence's head-pair launch
 hipError_t attn_cu_count(hipStream_t st, int* ncu);  // CUs of the stream's device (looked up once per device)
 // A sequence of a packed batch whose head-pair launch holds at least this

@@ -113,11 +113,11 @@ rr_status rr_pattern_search(const rr_problem* p, const void* q, const void* k,
  *               workspaces of their own.
  * Scale 1/sqrt(d); with p->causal, key y is visible to query x iff y <= x.
  * p->S and p->tau are not used but must be valid.
- * The kernel is chosen from the problem alone: bf16 with B = 128 and two or
- * more query heads per KV head runs two query heads per workgroup in a
- * ping-pong schedule (with an odd count the last head of every KV head is
+ * The kernel is chosen from the problem alone: bf16 with B = 128 runs two
+ * query heads per workgroup in a ping-pong schedule (with an odd count of
+ * query heads per KV head, one included, the last head of every KV head is
  * paired with itself over two adjacent query blocks in the same launch);
- * other bf16 shapes run one query head per workgroup; fp32 runs on the fp32
+ * bf16 with B = 64 runs one query head per workgroup; fp32 runs on the fp32
  * matrix cores.
  */
 rr_status rr_block_sparse_attn(const rr_problem* p, const void* q, const void* k, const void* v,
@@ -185,7 +185,7 @@ rr_status rr_share_group_lists(const rr_problem* p, const int32_t* row_count, co
  * offset sum_{b'<b} Hq nb_b', col_idx at sum_{b'<b} Hq nb_b'^2, with
  * nb_b = ceil(L_b / B). Every sequence's slices must stay 16-byte aligned
  * (else RR_ERR_UNSUPPORTED). Where the problem has the head-pair kernel
- * (bf16, B = 128, two or more query heads per KV head), the sequences run
+ * (bf16, B = 128), the sequences run
  * longest first: one with at least 8 attention work items per compute unit
  * (about 16K tokens at the LLaMA-3.1-8B shape on 256 CUs) is searched and
  * attended in launches of its own, as rr_prefill would; the others are

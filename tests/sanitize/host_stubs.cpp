@@ -98,7 +98,7 @@ hipError_t launch_union_lists(const Geometry&, const int32_t*, const int32_t*, i
   return hipSuccess;
 }
 
-bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128 && g.Hq / g.Hkv >= 2; }
+bool attn_pair_shape(const Geometry& g) { return g.bf16 && g.B == 128; }
 
 hipError_t attn_cu_count(hipStream_t, int* ncu) {
   *ncu = 256;

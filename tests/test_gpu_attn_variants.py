@@ -1,14 +1,18 @@
-"""GPU parity of the two bf16 attention kernels at B = 128 on the same lists.
+"""GPU parity of the head-pair attention kernel's two forms at B = 128 on the
+same lists.
 
-The library picks its kernel from the problem alone: with two or more query
-heads per KV head it launches the head-pair ping-pong kernel, with one it
-launches the one-head-per-workgroup kernel. Both therefore run on the same
-attention by posing it twice: once with the grouped K/V (ping-pong), once with
-K/V repeated per query head (Hkv = Hq, so G = 1 and the one-head kernel). Each
-is compared in full with the oracle's attention on the oracle's lists (bf16
-bars: max-abs 2e-2, mean-abs 2e-3), and the two outputs with each other
-within 1e-2 (both kernels share one softmax and walk a head's blocks in the
-same order; on these cases their outputs have in fact matched bit for bit).
+The library picks its kernel from the problem alone: bf16 with B = 128 runs
+the head-pair ping-pong kernel. Within a KV head it pairs two query heads;
+with an odd count (one query head per KV head included) the last head is
+paired with itself over two adjacent query blocks. Both forms therefore run
+on the same attention by posing it twice: once with the grouped K/V (heads
+paired), once with K/V repeated per query head (Hkv = Hq, so G = 1 and every
+head self-paired). Each is compared in full with the oracle's attention on
+the oracle's lists (bf16 bars: max-abs 2e-2, mean-abs 2e-3), and the two
+outputs with each other within 1e-2 (each head walks its blocks in the same
+order with the same softmax in both forms; on these cases their outputs
+have in fact matched bit for bit). The one-head kernel (B = 64) meets the
+oracle in the random problems below and in the ragged tests.
 
 A second test poses random problems (length, heads, head dimension, block
 size, causality, dtype) with random block lists, so that every kernel (head
@@ -35,7 +39,7 @@ from tests.gpu_cases import DeviceCase, say
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN = 2e-2, 2e-3
-VARIANTS = ["pingpong", "single_head"]
+VARIANTS = ["paired", "self_paired"]
 
 
 def g(name, L, Hq, Hkv, d, S, causal=True, kind="llm", seed=300):
@@ -52,9 +56,9 @@ CASES = [
 
 
 def run_variant(run, name, rc, ci):
-    """Attention of run's problem on the given lists through one kernel:
-    'pingpong' as posed, 'single_head' with K/V repeated per query head."""
-    if name == "pingpong":
+    """Attention of run's problem on the given lists in one form of the kernel:
+    'paired' as posed, 'self_paired' with K/V repeated per query head."""
+    if name == "paired":
         return run.attention(rc, ci)
     w = run.w
     G = w.Hq // w.Hkv
@@ -77,8 +81,8 @@ def test_attention_kernels_agree_with_oracle(w):
         say(f"  {name}: max-abs {mx:.3e} mean-abs {mean:.3e}")
         assert mx <= BF16_MAX and mean <= BF16_MEAN, name
         outs[name] = got
-    d = np.abs(outs["single_head"] - outs["pingpong"])
-    say(f"  single_head vs pingpong: max-abs {d.max():.3e}")
+    d = np.abs(outs["self_paired"] - outs["paired"])
+    say(f"  self_paired vs paired: max-abs {d.max():.3e}")
     assert d.max() <= 1e-2
 
 

@@ -176,6 +176,15 @@ def test_varlen_batch_matches_single_sequences():
     _varlen_case([1000, 2048, 300, 1537], 8, 2, 300)
 
 
+def test_varlen_batch_one_query_head_per_kv_head():
+    """MHA (G = 1) and an odd group (G = 3) in the batched launches: every head
+    of the first, and the last head of each KV head of the second, paired with
+    itself over two adjacent query blocks (the 257-token sequence has an odd
+    block count, so its lowest unit's lone head has no second block)."""
+    _varlen_case([1000, 2048, 300, 1537], 4, 4, 320)
+    _varlen_case([900, 1500, 257], 12, 4, 330)
+
+
 def test_varlen_long_sequence_in_its_own_launch():
     """17,000 tokens at the 8B shape hold 16 * 133 = 2,128 work items, over 8
     per CU on 256 CUs: that sequence gets a launch of its own, the two short
