@@ -146,6 +146,20 @@ int main() {
       }
       free(xws);
     }
+    {  // one query head per KV head (bf16, B = 128): batched like the grouped layers
+      rr_problem pg = {300 + 1000 + 128, 4, 4, 128, 16, 128, 0.9f, 1, RR_BF16};
+      const size_t gneed = rr_workspace_bytes_varlen(&pg, 3, lens);
+      void* gws = workspace(gneed);
+      const long b0 = g_stub.batched_launches;
+      EXPECT(rr_prefill_varlen(&pg, 3, lens, fake(1), fake(2), fake(7), fake(8), ifake(3), ifake(4), gws, gneed,
+                               nullptr),
+             RR_OK);
+      if (g_stub.batched_launches - b0 != 1) {
+        fprintf(stderr, "MHA varlen: %ld batched launches\n", g_stub.batched_launches - b0);
+        bad = 1;
+      }
+      free(gws);
+    }
     rr_problem pf = {300 + 1000 + 128, 4, 4, 64, 8, 64, 0.9f, 1, RR_FP32};  // per-sequence attention
     const size_t fneed = rr_workspace_bytes_varlen(&pf, 3, lens);
     void* fws = workspace(fneed);
