@@ -47,6 +47,8 @@ SMALL = [
     (g("gauss_b64_d128", 1024, 4, 1, 128, 8, 64, "bf16"), 0.85),
     (g("noncausal", 1024, 4, 2, 128, 16, 128, "bf16", causal=False), 0.9),
     (g("mha_g1_b128", 1024, 3, 3, 128, 16, 128, "bf16"), 0.9),
+    (g("llm_g8_d64", 2048, 16, 2, 64, 16, 128, "bf16", kind="llm"), 0.9),
+    (g("gauss_g16", 1024, 32, 2, 128, 16, 128, "bf16"), 0.9),
     (g("single_block", 128, 2, 1, 128, 16, 128, "bf16"), 0.9),
     (g("tau_one", 1024, 4, 2, 128, 16, 128, "bf16"), 1.0),
     (g("fp32_d128", 512, 4, 2, 128, 16, 128, "fp32"), 0.9),
