@@ -459,7 +459,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="llama8b_L128k")
+    ap.add_argument("--workload", default="llama8b_L128k",
+                    help="a named layer (synthetic.gen.WORKLOADS) or shape:L,Hq,Hkv,d,B,S[,dtype[,kind[,seed]]]")
     ap.add_argument("--tau", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-full", action="store_true",

@@ -91,6 +91,19 @@ WORKLOADS = {
 
 
 def workload(name: str) -> Workload:
+    """A named layer above, or any other shape as
+    `shape:L,Hq,Hkv,d,B,S[,dtype[,kind[,seed]]]` (defaults bf16, the LLaMA-like
+    recipe "llm" with one stripe key per 2,048 tokens (at least 8), seed 11;
+    tau 0.9; causal)."""
+    if name.startswith("shape:"):
+        f = name[len("shape:"):].split(",")
+        if len(f) < 6:
+            raise ValueError("shape:L,Hq,Hkv,d,B,S[,dtype[,kind[,seed]]] expected, got %r" % name)
+        L, Hq, Hkv, d, B, S = (int(x) for x in f[:6])
+        dtype = f[6] if len(f) > 6 else "bf16"
+        kind = f[7] if len(f) > 7 else "llm"
+        seed = int(f[8]) if len(f) > 8 else 11
+        return Workload(name, L, Hq, Hkv, d, dtype, B, S, (0.9,), seed, kind, max(8, L // 2048))
     return WORKLOADS[name]
 
 

@@ -87,3 +87,21 @@ def test_traffic_record_written_from_counter_runs(tmp_path, monkeypatch):
     assert abs(rec["mfma_busy"] - 0.5) < 1e-9
     # and bench reads it back while the source matches
     assert bench.measured_traffic("llama8b_L16k", 0.9) == (rec["traffic_bytes"], float(rec["algorithmic_bytes"]))
+
+
+def test_shape_workloads_parse():
+    """`--workload shape:L,Hq,Hkv,d,B,S[,dtype[,kind[,seed]]]` names any layer."""
+    from synthetic.gen import make_inputs, workload
+
+    w = workload("shape:4096,32,32,128,128,16")
+    assert (w.L, w.Hq, w.Hkv, w.d, w.B, w.S, w.dtype, w.kind, w.causal) == (4096, 32, 32, 128, 128, 16, "bf16",
+                                                                           "llm", True)
+    assert w.G == 1 and w.nb == 32 and w.taus == (0.9,)
+    w2 = workload("shape:300,4,2,64,64,8,fp32,gauss,5")
+    assert (w2.dtype, w2.kind, w2.seed, w2.nb) == ("fp32", "gauss", 5, 5)
+    q, k, v = make_inputs(w2)
+    assert tuple(q.shape) == (300, 4, 64) and tuple(k.shape) == (300, 2, 64) and str(q.dtype) == "torch.float32"
+    import pytest
+
+    with pytest.raises(ValueError):
+        workload("shape:4096,32,32")
